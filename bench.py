@@ -1,0 +1,212 @@
+"""Benchmark of the fused head-dim-64 attention library on one MI355X.
+
+One JSON line on stdout.  A step is one call of the dense flash kernel on the
+SDXL level-1 self-attention workload (bf16, B=2, H=10, S=4096, D=64); `value` is
+its attention TFLOP/s (4*D flops per query-key pair, inputs already in HBM).  The
+other forms of the hot path -- cross-attention against 77 keys, banded and full
+differential attention -- are timed the same way and reported under "forms",
+each against its own roofline (MFMA for the dense forms, HBM for the banded one).
+Kernel time is measured with HIP events recorded on the stream the kernels run
+on.  HBM-bound forms rotate several input copies so that the 256 MB last-level
+cache does not serve them.  The fp64 CPU oracle is timed on a bounded sample of
+the same workload for `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from head_attention_flash_amd import accounting as acc  # noqa: E402
+from head_attention_flash_amd import synth  # noqa: E402
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def up(x, torch):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def time_launches(fn, nsets, steps, warmup, torch):
+    """Average seconds per launch over `steps` launches, rotating over `nsets` input sets."""
+    for i in range(warmup):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(i % nsets)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, launch_units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still matches the source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_digest") != source_digest(ent.get("sources", [])):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on the whole dense workload (every query row, all keys), in TFLOP/s."""
+    import oracle
+    q, k, v = synth.make_dense(wl)
+    lib = oracle.load()
+    qd, kd, vd = (oracle.widen(x) for x in (q, k, v))  # widening is marshalling, kept outside the timing
+    t0 = time.perf_counter()
+    oracle.attn(qd, kd, vd, wl.scale, lib=lib)
+    dt = time.perf_counter() - t0
+    flops = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole {wl.key} workload ({wl.B * wl.H * wl.Sq} query rows x {wl.Sk} keys), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forms", default="cross,band,full", help="extra forms to time (comma list, or 'none')")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_attention_flash_amd as ka
+    from head_attention_flash_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    ka.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    # ---------------- headline: dense self-attention, SDXL level 1
+    wl = synth.WORKLOADS["sdxl_l1_self_b2h10s4096"]
+    log(f"bench: {wl.desc}")
+    q, k, v = (up(x, torch) for x in synth.make_dense(wl))
+    o = torch.empty_like(q)
+    flops = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk)
+
+    def step(_):
+        ka.ka_attn_fwd(q, k, v, o=o, scale=wl.scale)
+
+    torch.cuda.synchronize()
+    sec = time_launches(step, 1, args.steps, args.warmup, torch)
+    value = flops / sec / 1e12
+    log(f"bench: dense {sec * 1e6:.1f} us/launch, {value:.1f} TFLOP/s")
+    traffic = traffic_for("attn_bf16_flash", 1)
+    result = {
+        "metric": "attention TFLOP/s (% MFMA peak) dense; GB/s (% HBM peak) banded diff-attn",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1), no dataset)",
+        "config": {"workload": wl.key, "form": "dense self-attention", "B": wl.B, "H": wl.H, "Sq": wl.Sq,
+                   "Sk": wl.Sk, "D": 64, "scale": wl.scale},
+        "roofline": {"bound": "mfma", "achieved": round(flops / sec / 1e12, 3),
+                     "peak": acc.MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": round(flops / sec / acc.MFMA_BF16_PEAK, 4), "traffic": traffic,
+                     "kernel": "attn_bf16_flash", "flops_per_launch": flops},
+    }
+    del q, k, v, o
+
+    forms = {}
+    wanted = set() if args.forms == "none" else set(args.forms.split(","))
+    # ---------------- cross-attention against 77 keys (HBM-bound: rotate 8 input copies)
+    if "cross" in wanted:
+        wl = synth.WORKLOADS["sdxl_l2_cross_b2h20q1024k77"]
+        log(f"bench: {wl.desc}")
+        sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s)] for s in range(8)]
+        outs = [torch.empty_like(s[0]) for s in sets]
+        f, b = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk), acc.dense_bytes(wl.B, wl.H, wl.Sq, wl.Sk)
+        sec = time_launches(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
+                            args.warmup, torch)
+        forms["cross"] = {"workload": wl.key, "kernel": "xattn_bf16", "us": round(sec * 1e6, 3),
+                          "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
+                          "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
+                          "bound": "hbm", "flops": f, "bytes": b, "input_copies": len(sets)}
+        log(f"bench: cross {forms['cross']}")
+        del sets, outs
+    # ---------------- banded differential attention (HBM-bound: 3 copies = 425 MB > 256 MB cache)
+    if "band" in wanted:
+        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
+        log(f"bench: {wl.desc}")
+        sets = []
+        for s in range(3):
+            ins, prm = synth.make_diff(wl, seed_base=1000 * wl.index + 10 * s)
+            sets.append(([up(x, torch) for x in ins], [up(x, torch) for x in prm]))
+        outs = [torch.empty_like(s[0][0]) for s in sets]
+        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
+
+        def band(i):
+            ins, (a_, g_, b_, l_) = sets[i]
+            ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window)
+
+        sec = time_launches(band, len(sets), args.steps, args.warmup, torch)
+        forms["band_diff"] = {"workload": wl.key, "kernel": "diff_band", "us": round(sec * 1e6, 3),
+                              "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
+                              "TFLOP/s": round(f / sec / 1e12, 3), "bound": "hbm", "flops": f, "bytes": b,
+                              "input_copies": len(sets), "traffic": traffic_for("diff_band", 1)}
+        log(f"bench: band {forms['band_diff']}")
+        del sets, outs
+    # ---------------- full differential attention (DiT-shaped)
+    if "full" in wanted:
+        wl = synth.WORKLOADS["sa3_dit_fulldiff_h16s1422"]
+        log(f"bench: {wl.desc}")
+        ins, prm = synth.make_diff(wl)
+        ins = [up(x, torch) for x in ins]
+        a_, g_, b_, l_ = (up(x, torch) for x in prm)
+        o = torch.empty_like(ins[0])
+        ws = torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
+                         device="cuda")
+        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
+        sec = time_launches(lambda i: ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=o, scale=wl.scale,
+                                                         window=wl.window, workspace=ws),
+                            1, args.steps, args.warmup, torch)
+        forms["full_diff"] = {"workload": wl.key, "kernel": "diff_kprep + diff_flash", "us": round(sec * 1e6, 3),
+                              "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
+                              "GB/s": round(b / sec / 1e9, 1), "bound": "mfma", "flops": f, "bytes": b}
+        log(f"bench: full {forms['full_diff']}")
+    if forms:
+        result["forms"] = forms
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(synth.WORKLOADS["sdxl_l1_self_b2h10s4096"])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""Thin ctypes binding of libka_attn.so: argument marshalling only.
+
+The functions carry the C names.  They take torch tensors that already live on
+the GPU (torch only allocates memory and supplies the stream), pass their data
+pointers and the current HIP stream to the C ABI, and raise KaError on any
+non-OK status.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: if the library is not built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libka_attn.so")
+
+KA_OK, KA_ERR_NULL, KA_ERR_SHAPE, KA_ERR_UNSUPPORTED, KA_ERR_PARAM, KA_ERR_ALIGN, KA_ERR_ALIAS, \
+    KA_ERR_WORKSPACE, KA_ERR_HIP = range(9)
+KA_F32, KA_BF16 = 0, 1
+KA_XATTN_MAX_SK = 256
+
+# every symbol include/ka_attn.h declares
+EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_workspace_bytes", "ka_status_string",
+           "ka_last_hip_error", "ka_version")
+
+
+class KaError(RuntimeError):
+    def __init__(self, status: int, where: str, lib=None):
+        msg = lib.ka_status_string(status).decode() if lib is not None else str(status)
+        extra = f" (hipError {lib.ka_last_hip_error()})" if (lib is not None and status == KA_ERR_HIP) else ""
+        super().__init__(f"{where}: {msg}{extra}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libka_attn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.ka_attn_fwd.argtypes = [i, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.ka_attn_fwd.restype = i
+    lib.ka_xattn_fwd.argtypes = [i, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.ka_xattn_fwd.restype = i
+    lib.ka_diffattn_fwd.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, f, vp, vp, sz, vp]
+    lib.ka_diffattn_fwd.restype = i
+    lib.ka_diffattn_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.ka_diffattn_workspace_bytes.restype = sz
+    lib.ka_status_string.argtypes = [i]
+    lib.ka_status_string.restype = ctypes.c_char_p
+    lib.ka_last_hip_error.argtypes = []
+    lib.ka_last_hip_error.restype = i
+    lib.ka_version.argtypes = []
+    lib.ka_version.restype = ctypes.c_char_p
+    del fp
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return KA_F32
+    if t.dtype == torch.bfloat16:
+        return KA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, S, D]")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(lib, st: int, where: str):
+    if st != KA_OK:
+        raise KaError(st, where, lib)
+
+
+def ka_attn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
+    """Dense attention; q [B,H,Sq,64], k/v [B,H,Sk,64] (fp32 or bf16, same dtype). Returns o."""
+    lib = load()
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if o is None:
+        o = _torch().empty_like(q)
+    st = lib.ka_attn_fwd(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, H, Sq, Sk, D,
+                         float(scale), _stream(stream))
+    _check(lib, st, "ka_attn_fwd")
+    return o
+
+
+def ka_xattn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
+    """Cross-attention against a short key set (Sk <= 256) held on chip. Returns o."""
+    lib = load()
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if o is None:
+        o = _torch().empty_like(q)
+    st = lib.ka_xattn_fwd(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), B, H, Sq, Sk, D,
+                          float(scale), _stream(stream))
+    _check(lib, st, "ka_xattn_fwd")
+    return o
+
+
+def ka_diffattn_workspace_bytes(B: int, H: int, S: int, D: int = 64, window: int = -1) -> int:
+    return int(load().ka_diffattn_workspace_bytes(B, H, S, D, window))
+
+
+def ka_diffattn_fwd(q1, k1, q2, k2, v, alpha, gamma, beta, lam, o=None, scale: float = 0.125, window: int = -1,
+                    rope_base: float = 10000.0, workspace=None, stream=None):
+    """Differential attention (bf16). alpha [4], gamma/beta [4,64], lam [H]: fp32 GPU tensors.
+
+    workspace: a GPU uint8 tensor of at least ka_diffattn_workspace_bytes(...) bytes, or None to
+    have torch allocate one for this call.
+    """
+    lib = load()
+    B, H, S, D = q1.shape
+    if o is None:
+        o = _torch().empty_like(q1)
+    need = int(lib.ka_diffattn_workspace_bytes(B, H, S, D, window))
+    if workspace is None and need:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q1.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.ka_diffattn_fwd(_dtype_code(q1), _dev(q1, "q1"), _dev(k1, "k1"), _dev(q2, "q2"), _dev(k2, "k2"),
+                             _dev(v, "v"), _dev(o, "o"), B, H, S, S, D, float(scale), int(window),
+                             _dev(alpha, "alpha"), _dev(gamma, "gamma"), _dev(beta, "beta"), float(rope_base),
+                             _dev(lam, "lambda"), ws_ptr, ws_bytes, _stream(stream))
+    _check(lib, st, "ka_diffattn_fwd")
+    return o

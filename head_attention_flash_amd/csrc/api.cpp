@@ -1,0 +1,167 @@
+// api.cpp -- the C ABI of libka_attn: validation on the host, then one launch
+// sequence on the caller's stream.  No allocation, no synchronisation, no state
+// beyond a thread-local copy of the last HIP error.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ka_attn.h"
+#include "ka_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+ka_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KA_OK;
+  g_last_hip_error = (int)e;
+  return KA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p + n) and [q, q + m) overlap
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return n && m && a < b + m && b < a + n;
+}
+
+// B*H*S*D*elem without overflowing 64 bits (and each tensor below 2^62 bytes).
+bool tensor_bytes(int B, int H, int S, int D, size_t elem, size_t* out) {
+  unsigned __int128 n = (unsigned __int128)(unsigned)B * (unsigned)H * (unsigned)S * (unsigned)D * elem;
+  if (n >> 62) return false;
+  *out = (size_t)n;
+  return true;
+}
+
+ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                      int Sk, int D, float scale, size_t* qbytes, size_t* kbytes) {
+  if (!q || !k || !v || !o) return KA_ERR_NULL;
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return KA_ERR_SHAPE;
+  if (D != 64) return KA_ERR_UNSUPPORTED;
+  if (dt != KA_F32 && dt != KA_BF16) return KA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return KA_ERR_PARAM;
+  const size_t e = dt == KA_F32 ? 4 : 2;
+  if (!tensor_bytes(B, H, Sq, D, e, qbytes) || !tensor_bytes(B, H, Sk, D, e, kbytes)) return KA_ERR_SHAPE;
+  // the grid's y dimension carries B*H
+  if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KA_ERR_ALIGN;
+  if (overlap(o, *qbytes, q, *qbytes) || overlap(o, *qbytes, k, *kbytes) || overlap(o, *qbytes, v, *kbytes))
+    return KA_ERR_ALIAS;
+  return KA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                      int Sk, int D, float scale, hipStream_t stream) {
+  size_t qb = 0, kb = 0;
+  ka_status st = check_dense(dtype, q, k, v, o, B, H, Sq, Sk, D, scale, &qb, &kb);
+  if (st != KA_OK) return st;
+  if (dtype == KA_F32)
+    return hip_status(ka::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                          static_cast<const float*>(v), static_cast<float*>(o), B, H, Sq, Sk, scale,
+                                          stream));
+  return hip_status(ka::launch_attn_bf16(static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                                         static_cast<const unsigned short*>(v), static_cast<unsigned short*>(o), B, H,
+                                         Sq, Sk, scale, stream));
+}
+
+ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                       int Sk, int D, float scale, hipStream_t stream) {
+  size_t qb = 0, kb = 0;
+  ka_status st = check_dense(dtype, q, k, v, o, B, H, Sq, Sk, D, scale, &qb, &kb);
+  if (st != KA_OK) return st;
+  if (Sk > KA_XATTN_MAX_SK) return KA_ERR_SHAPE;
+  if (dtype == KA_F32)
+    return hip_status(ka::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                          static_cast<const float*>(v), static_cast<float*>(o), B, H, Sq, Sk, scale,
+                                          stream));
+  return hip_status(ka::launch_xattn_bf16(static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                                          static_cast<const unsigned short*>(v), static_cast<unsigned short*>(o), B,
+                                          H, Sq, Sk, scale, stream));
+}
+
+size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window) {
+  size_t n = 0;
+  if (B < 1 || H < 1 || S < 1 || D != 64 || !tensor_bytes(B, H, S, D, 2, &n)) return 0;
+  return ka::diff_workspace_bytes(B, H, S, window);
+}
+
+ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                          const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                          const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta, float rope_base,
+                          const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q1 || !k1 || !q2 || !k2 || !v || !o || !dyt_alpha || !dyt_gamma || !dyt_beta || !lambda) return KA_ERR_NULL;
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || Sq != Sk) return KA_ERR_SHAPE;
+  if (D != 64 || dtype != KA_BF16) return KA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(rope_base) || !(rope_base > 1.0f))
+    return KA_ERR_PARAM;
+  const int S = Sq;
+  size_t tb = 0;
+  if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
+  if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  const void* ins[5] = {q1, k1, q2, k2, v};
+  for (const void* p : ins)
+    if (!aligned16(p)) return KA_ERR_ALIGN;
+  if (!aligned16(o)) return KA_ERR_ALIGN;
+  const size_t need = ka::diff_workspace_bytes(B, H, S, window);
+  if (need) {
+    if (!workspace) return KA_ERR_NULL;
+    if (workspace_bytes < need) return KA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KA_ERR_ALIGN;
+  }
+  for (const void* p : ins)
+    if (overlap(o, tb, p, tb)) return KA_ERR_ALIAS;
+  if (need && overlap(o, tb, workspace, need)) return KA_ERR_ALIAS;
+  if (need)
+    for (const void* p : ins)
+      if (overlap(workspace, need, p, tb)) return KA_ERR_ALIAS;
+
+  ka::DiffArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q1 = static_cast<const unsigned short*>(q1);
+  a.k1 = static_cast<const unsigned short*>(k1);
+  a.q2 = static_cast<const unsigned short*>(q2);
+  a.k2 = static_cast<const unsigned short*>(k2);
+  a.v = static_cast<const unsigned short*>(v);
+  a.o = static_cast<unsigned short*>(o);
+  a.ws = static_cast<_Float16*>(workspace);
+  a.alpha = dyt_alpha;
+  a.gamma = dyt_gamma;
+  a.beta = dyt_beta;
+  a.lambda = lambda;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.window = window < 0 ? -1 : window;
+  a.c = scale * 1.4426950408889634f;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < 32; ++i) a.rev[i] = std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi;
+  return hip_status(ka::launch_diffattn(a, stream));
+}
+
+const char* ka_status_string(ka_status s) {
+  switch (s) {
+    case KA_OK: return "ok";
+    case KA_ERR_NULL: return "null pointer";
+    case KA_ERR_SHAPE: return "invalid shape";
+    case KA_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
+    case KA_ERR_PARAM: return "invalid scalar parameter";
+    case KA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KA_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case KA_ERR_WORKSPACE: return "workspace too small";
+    case KA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int ka_last_hip_error(void) { return g_last_hip_error; }
+
+const char* ka_version(void) { return "0.1.0"; }
+
+}  // extern "C"

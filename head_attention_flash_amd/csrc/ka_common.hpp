@@ -1,0 +1,128 @@
+// ka_common.hpp -- building blocks shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (v_mfma_f32_16x16x32_{bf16,f16}, wave64), as used by
+// every kernel here:
+//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) + e   (e = 0..7)
+//   B (32 x 16): lane l holds column l%16, k = 8*(l/16) + e
+//   C (16 x 16): lane l holds column l%16, rows 4*(l/16) + e (e = 0..3)
+// The kernels compute S^T = K Q^T and O^T = V^T P^T so that one lane owns one
+// query column: the softmax statistics of a query live in a single lane group
+// and the rescale of O is a per-lane scalar.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ka {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int HD = 64;                 // head dim this library is built for
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Reduction over the four lanes {l, l^16, l^32, l^48} (the four row groups of a
+// C tile that hold the same query column).  permlane16_swap(x, x) yields the
+// even-row and odd-row copies of each 16-lane pair; permlane32_swap(x, x) the
+// lower and upper halves.
+__device__ __forceinline__ float group4_max(float x) {
+  u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  u32x2 b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
+// receives slot e = element (i%4) of the 8 bytes addressed by source lane 4e + i/4.
+// With source lane s pointing at row r(s/4), column c0 + 4*(s%4) of a row-major
+// 16-bit matrix, lane i gets column c0 + i of rows r(0..3).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat_bf16(i16x4 lo, i16x4 hi) {
+  bf16x8 r;
+  bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Pack 4 + 4 fp32 values into one bf16x8 MFMA operand (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// Unpack 8 bf16 (one uint4) into fp32.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Four fp32 -> four bf16 packed into 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16_bits(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Parameters of the DyT + rotary preparation of one tensor (q1, k1, q2 or k2).
+struct PrepParams {
+  float k2a;          // 2 * log2(e) * alpha: tanh(alpha x) = 1 - 2 / (1 + 2^(k2a x))
+};
+
+// DyT: gamma * tanh(alpha * x) + beta, with tanh(y) = 1 - 2/(1 + e^{2y}).
+// Saturates correctly: e^{2y} -> inf gives 1, -> 0 gives -1.
+__device__ __forceinline__ float dyt(float x, float k2a, float gamma, float beta) {
+  float e = fast_exp2(k2a * x);
+  float r = __builtin_amdgcn_rcpf(1.0f + e);
+  float t = __builtin_fmaf(-2.0f, r, 1.0f);
+  return __builtin_fmaf(gamma, t, beta);
+}
+
+// Rotary angle of (position p, pair i) as cos/sin.  The angle in revolutions,
+// p * f_i / (2 pi), is formed and reduced to [-1/2, 1/2] in fp64 (an fp32 product
+// at p ~ 2e4 would be off by ~1e-3 rad); the hardware sin/cos take revolutions.
+__device__ __forceinline__ void rope_cs(int p, double rev_per_pos, float& c, float& s) {
+  double t = (double)p * rev_per_pos;
+  t -= __builtin_rint(t);
+  float f = (float)t;
+  c = __builtin_amdgcn_cosf(f);
+  s = __builtin_amdgcn_sinf(f);
+}
+
+}  // namespace ka

@@ -1,0 +1,42 @@
+// ka_kernels.hpp -- launchers of the gfx950 kernels (internal to the library).
+// Each launcher enqueues on `s` and returns hipGetLastError(); shapes were
+// validated by the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ka {
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, int B, int H, int Sq, int Sk,
+                           float scale, hipStream_t s);
+hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
+                            unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s);
+hipError_t launch_xattn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
+                             unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s);
+
+// Everything the differential kernels need, passed by value.
+struct DiffArgs {
+  const unsigned short* q1;
+  const unsigned short* k1;
+  const unsigned short* q2;
+  const unsigned short* k2;
+  const unsigned short* v;
+  unsigned short* o;
+  _Float16* ws;            // prepared keys (full path): [2][B][H][S][64] fp16
+  const float* alpha;      // [4]
+  const float* gamma;      // [4][64]
+  const float* beta;       // [4][64]
+  const float* lambda;     // [H]
+  int B, H, S;
+  int window;              // >= 0: |i - j| <= window; < 0: all keys
+  float c;                 // scale * log2(e)
+  double rev[32];          // rope_base^(-2i/64) / (2 pi): revolutions per position of pair i
+};
+
+// Largest window the one-pass band kernel takes; wider windows use the flash path.
+constexpr int BAND_MAX_WINDOW = 40;
+
+size_t diff_workspace_bytes(int B, int H, int S, int window);
+hipError_t launch_diffattn(const DiffArgs& a, hipStream_t s);
+
+}  // namespace ka

@@ -1,0 +1,124 @@
+/*
+ * ka_attn.h -- fused head-dim-64 attention for AMD MI355X (gfx950): the C ABI.
+ *
+ * Three operations, each one fused HIP kernel launch sequence enqueued on the
+ * caller's stream:
+ *
+ *   ka_attn_fwd      dense scaled-dot-product attention (flash / online softmax)
+ *   ka_xattn_fwd     cross-attention against a short key set held on chip
+ *   ka_diffattn_fwd  differential attention with DyT and rotary embedding on Q/K,
+ *                    banded (+-window keys) or full
+ *
+ * Common conventions
+ *   - Pointers q, k, v, q1, k1, q2, k2, o, the parameter arrays and the
+ *     workspace are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees, synchronises or keeps a pointer after the call returns.
+ *   - Every activation tensor is contiguous row-major [B][H][S][D] (D innermost);
+ *     o has the layout of q.  D must be 64.
+ *   - Data types: KA_F32 (float32 in, float32 out, float32 arithmetic) or
+ *     KA_BF16 (bfloat16 in, bfloat16 out; matrix products on bf16/fp16 MFMA with
+ *     float32 accumulation; softmax, DyT, rotary embedding and the branch
+ *     subtraction in float32).
+ *   - Work is enqueued on `stream` and nothing else; the call returns without
+ *     waiting.  Results are bitwise deterministic (no atomics).  The library has
+ *     no mutable global state, so concurrent calls on different streams are safe.
+ *   - Arguments are validated on the host before any HIP call; on failure
+ *     nothing is enqueued and a status code is returned.  A failed launch
+ *     returns KA_ERR_HIP and ka_last_hip_error() holds the hipError_t (per
+ *     thread).  No C++ exception crosses this interface.
+ *   - Inputs with NaN or Inf are outside the contract (they propagate).
+ */
+#ifndef KA_ATTN_H
+#define KA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KA_OK = 0,
+  KA_ERR_NULL = 1,         /* a required pointer is NULL                                  */
+  KA_ERR_SHAPE = 2,        /* a dimension < 1, Sq != Sk on the diff path, Sk above the
+                              cross-attention limit, or a size overflowing 64 bits        */
+  KA_ERR_UNSUPPORTED = 3,  /* D != 64, or a dtype this entry point does not take          */
+  KA_ERR_PARAM = 4,        /* non-finite or non-positive scale, rope_base <= 1 or not
+                              finite                                                      */
+  KA_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned                     */
+  KA_ERR_ALIAS = 6,        /* o overlaps an input or the workspace                        */
+  KA_ERR_WORKSPACE = 7,    /* workspace smaller than ka_diffattn_workspace_bytes()        */
+  KA_ERR_HIP = 8           /* a HIP call failed; see ka_last_hip_error()                  */
+} ka_status;
+
+typedef enum { KA_F32 = 0, KA_BF16 = 1 } ka_dtype;
+
+/* Largest key count ka_xattn_fwd holds on chip. */
+#define KA_XATTN_MAX_SK 256
+
+/*
+ * Dense scaled-dot-product attention, no mask.
+ * Definition ("SDXL as a requirements inventory", s1.3, CrossAttention): for
+ * every (b, h, i),
+ *     o[b,h,i,:] = sum_j softmax_j(scale * <q[b,h,i,:], k[b,h,j,:]>) v[b,h,j,:]
+ * with j over [0, Sk).  SDXL uses scale = 64^-1/2 = 0.125.
+ *   q [B,H,Sq,D], k and v [B,H,Sk,D], o [B,H,Sq,D]; dtype KA_F32 or KA_BF16.
+ *   Any B, H, Sq, Sk >= 1.
+ */
+ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                      int Sk, int D, float scale, hipStream_t stream);
+
+/*
+ * Cross-attention: the same definition as ka_attn_fwd, for a short key set
+ * (1 <= Sk <= KA_XATTN_MAX_SK, e.g. SDXL's 77 text-context tokens, "SDXL as a
+ * requirements inventory" s1.2 and s5.7).  All Sk keys and values of a (b, h)
+ * are held in LDS and re-read by every query tile; queries stream through.
+ *   dtype KA_BF16 (KA_F32 is accepted and routed to the fp32 kernel).
+ */
+ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
+                       int Sk, int D, float scale, hipStream_t stream);
+
+/*
+ * Differential attention with DyT and rotary embedding
+ * ("401 -> 163 ms: Stable Audio 3 medium on one TPU v6e chip", s3, s5 and
+ * appendix E1, E2, D4).  For every (b, h, p), with t in {q1, k1, q2, k2} and
+ * set index 0..3 in that order:
+ *   DyT:   x~ = gamma_t[d] * tanh(alpha_t * x[d]) + beta_t[d]            (fp32)
+ *   RoPE:  rotate-half over all 64 dims at position p (token index):
+ *          theta_i = p * rope_base^(-2i/64), i < 32,
+ *          y[i]    = x~[i] cos theta_i - x~[i+32] sin theta_i,
+ *          y[i+32] = x~[i+32] cos theta_i + x~[i] sin theta_i
+ *   branch r = 1, 2:  O_r = sum_{j in W(p)} softmax_j(scale <q^_r[p], k^_r[j]>) v[j]
+ *   output:           o[b,h,p,:] = O_1 - lambda[h] * O_2
+ * W(p) = { j in [0, S) : |j - p| <= window } when window >= 0 (keys outside
+ * [0, S) are absent, not zero), every j when window < 0.
+ *   q1, k1, q2, k2, v, o: [B,H,S,D] bf16 (Sq must equal Sk = S); dtype KA_BF16.
+ *   dyt_alpha [4], dyt_gamma [4][64], dyt_beta [4][64], lambda [H]: fp32 device.
+ *   workspace: device scratch of at least ka_diffattn_workspace_bytes(B,H,S,D,
+ *   window) bytes (may be NULL when that is 0); its contents are overwritten.
+ */
+ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                          const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                          const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta, float rope_base,
+                          const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ka_diffattn_fwd needs for this shape (0 for the banded path).
+ * Returns 0 for invalid shapes as well; ka_diffattn_fwd then reports the error. */
+size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window);
+
+/* Static description of a status code. */
+const char* ka_status_string(ka_status status);
+
+/* hipError_t of the last KA_ERR_HIP returned on the calling thread (0 if none). */
+int ka_last_hip_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* ka_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KA_ATTN_H */

@@ -1,0 +1,130 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares, and rejects bad
+arguments with the documented status codes before touching HIP (no compute call is made here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import head_attention_flash_amd as ka
+from head_attention_flash_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ka_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ka_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_operations():
+    syms = declared_symbols()
+    for s in ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), f"{s} declared in ka_attn.h but not exported"
+    assert set(declared_symbols()) == set(_lib.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert re.match(rb"^\d+\.\d+\.\d+$", lib.ka_version())
+    for st in range(9):
+        assert lib.ka_status_string(st)
+    assert lib.ka_status_string(99) == b"unknown status"
+    assert lib.ka_last_hip_error() == 0
+
+
+# fake, distinct, 16-byte aligned device addresses: only validation runs on them
+Q, K, V, O, O2, A, G, BT, L, W = (0x100000 * (i + 1) for i in range(10))
+
+
+def dense(lib, fn, dt=ka.KA_BF16, q=Q, k=K, v=V, o=O, B=1, H=1, Sq=4, Sk=4, D=64, scale=0.125):
+    f = getattr(lib, fn)
+    return f(dt, q, k, v, o, B, H, Sq, Sk, D, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("fn", ["ka_attn_fwd", "ka_xattn_fwd"])
+def test_dense_validation(lib, fn):
+    assert dense(lib, fn, q=0) == _lib.KA_ERR_NULL
+    assert dense(lib, fn, o=0) == _lib.KA_ERR_NULL
+    assert dense(lib, fn, B=0) == _lib.KA_ERR_SHAPE
+    assert dense(lib, fn, H=-1) == _lib.KA_ERR_SHAPE
+    assert dense(lib, fn, Sq=0) == _lib.KA_ERR_SHAPE
+    assert dense(lib, fn, Sk=0) == _lib.KA_ERR_SHAPE
+    assert dense(lib, fn, D=128) == _lib.KA_ERR_UNSUPPORTED
+    assert dense(lib, fn, dt=7) == _lib.KA_ERR_UNSUPPORTED
+    assert dense(lib, fn, scale=float("nan")) == _lib.KA_ERR_PARAM
+    assert dense(lib, fn, scale=math.inf) == _lib.KA_ERR_PARAM
+    assert dense(lib, fn, scale=0.0) == _lib.KA_ERR_PARAM
+    assert dense(lib, fn, q=Q + 8) == _lib.KA_ERR_ALIGN
+    assert dense(lib, fn, o=O + 2) == _lib.KA_ERR_ALIGN
+    assert dense(lib, fn, o=Q) == _lib.KA_ERR_ALIAS
+    assert dense(lib, fn, o=K + 256) == _lib.KA_ERR_ALIAS
+    assert dense(lib, fn, B=1 << 20, H=1 << 20, Sq=1 << 20) == _lib.KA_ERR_SHAPE  # bytes overflow
+    assert lib.ka_last_hip_error() == 0
+
+
+def test_xattn_key_limit(lib):
+    assert dense(lib, "ka_xattn_fwd", Sk=ka.KA_XATTN_MAX_SK + 1) == _lib.KA_ERR_SHAPE
+
+
+def diff(lib, dt=ka.KA_BF16, q1=Q, k1=K, q2=V, k2=O2, v=A, o=O, B=1, H=2, Sq=8, Sk=8, D=64, scale=0.125, window=2,
+         alpha=A + 0x80000, gamma=G, beta=BT, base=10000.0, lam=L, ws=0, ws_bytes=0):
+    return lib.ka_diffattn_fwd(dt, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, ctypes.c_float(scale), window, alpha, gamma,
+                               beta, ctypes.c_float(base), lam, ws, ws_bytes, None)
+
+
+def test_diff_validation(lib):
+    for name in ("q1", "k1", "q2", "k2", "v", "o", "alpha", "gamma", "beta", "lam"):
+        assert diff(lib, **{name: 0}) == _lib.KA_ERR_NULL, name
+    assert diff(lib, Sk=9) == _lib.KA_ERR_SHAPE
+    assert diff(lib, B=0) == _lib.KA_ERR_SHAPE
+    assert diff(lib, D=32) == _lib.KA_ERR_UNSUPPORTED
+    assert diff(lib, dt=ka.KA_F32) == _lib.KA_ERR_UNSUPPORTED
+    assert diff(lib, base=1.0) == _lib.KA_ERR_PARAM
+    assert diff(lib, base=float("inf")) == _lib.KA_ERR_PARAM
+    assert diff(lib, scale=-1.0) == _lib.KA_ERR_PARAM
+    assert diff(lib, v=A + 4) == _lib.KA_ERR_ALIGN
+    assert diff(lib, o=Q + 64) == _lib.KA_ERR_ALIAS
+    # the full path needs a workspace
+    need = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
+    assert need == 2 * 1 * 2 * 8 * 64 * 2
+    assert diff(lib, window=-1) == _lib.KA_ERR_NULL
+    assert diff(lib, window=-1, ws=W, ws_bytes=need - 1) == _lib.KA_ERR_WORKSPACE
+    assert diff(lib, window=-1, ws=W + 8, ws_bytes=need) == _lib.KA_ERR_ALIGN
+    assert diff(lib, window=-1, ws=O, ws_bytes=need) == _lib.KA_ERR_ALIAS
+    assert diff(lib, window=-1, ws=K, ws_bytes=need) == _lib.KA_ERR_ALIAS
+    assert lib.ka_last_hip_error() == 0
+
+
+def test_workspace_sizes(lib):
+    # banded windows the one-pass kernel takes need no workspace
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 23086, 64, 17) == 0
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 23086, 64, 40) == 0
+    # wide windows and the full window prepare keys once into the workspace
+    assert lib.ka_diffattn_workspace_bytes(1, 16, 1422, 64, -1) == 2 * 16 * 1422 * 64 * 2
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 100, 64, 41) == 2 * 8 * 100 * 64 * 2
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 30, 64, 29) == 2 * 8 * 30 * 64 * 2  # window >= S-1: full
+    assert lib.ka_diffattn_workspace_bytes(0, 8, 100, 64, -1) == 0
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 100, 32, -1) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        ka.ka_attn_fwd(x, x, x, o=torch.zeros_like(x))

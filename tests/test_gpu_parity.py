@@ -1,0 +1,218 @@
+"""GPU parity: every form of the library, through the C ABI, against the fp64 oracle.
+
+Small cases are compared element by element on every output; the full-size
+workloads (the ones the bench times, in the same launch configuration) are
+compared on sampled rows that the oracle computes one by one.  Tolerances: max
+abs error 2e-2 for bf16 in/out (fp32 accumulation) and 1e-4 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_attention_flash_amd as ka
+import oracle
+from gpu_util import BF16_TOL, F32_TOL, assert_close, diff_params_dev, nan_like, to_dev, to_host_f64
+from head_attention_flash_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+D = 64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ka.load()
+
+
+def _rows_sample(B, H, S, n, seed, edge=0, period=0):
+    """Flat row indices: n random rows plus, per (b, h), `edge` rows at each end and rows at period boundaries."""
+    r = np.random.default_rng(seed)
+    rows = set(r.integers(0, B * H * S, n).tolist())
+    for bh in range(B * H):
+        for p in list(range(min(edge, S))) + list(range(max(0, S - edge), S)):
+            rows.add(bh * S + p)
+        if period:
+            for p in range(period, S, period):
+                for d in (-1, 0):
+                    if 0 <= p + d < S and r.random() < 0.25:
+                        rows.add(bh * S + p + d)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ dense
+
+def _run_dense(fn, q, k, v, scale=0.125):
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    o = nan_like(qd)  # every output element must be written exactly once
+    fn(qd, kd, vd, o=o, scale=scale)
+    torch.cuda.synchronize()
+    return to_host_f64(o)
+
+
+def test_dense_f32_workload():
+    wl = W["dense_f32_b1h2s256"]
+    q, k, v = synth.make_dense(wl)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale)
+    assert_close(got, oracle.attn(q, k, v, wl.scale), F32_TOL, wl.key)
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk", [(1, 1, 1, 1), (1, 3, 77, 130), (2, 1, 129, 33), (1, 1, 300, 1000)])
+def test_dense_f32_ragged(B, H, Sq, Sk):
+    wl = W["dense_f32_b1h2s256"]
+    q, k, v = synth.make_dense(wl, seed_base=Sq * 7 + Sk, B=B, H=H, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), F32_TOL, f"f32 {B}x{H}x{Sq}x{Sk}")
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk", [(1, 2, 200, 333), (1, 1, 1, 1), (1, 1, 16, 64), (1, 1, 65, 65),
+                                       (2, 3, 129, 257), (1, 1, 64, 4096), (1, 2, 1000, 1000)])
+def test_dense_bf16_shapes(B, H, Sq, Sk):
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = synth.make_dense(wl, seed_base=100 + Sq + Sk, B=B, H=H, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"bf16 {B}x{H}x{Sq}x{Sk}")
+
+
+def test_dense_bf16_peaked():
+    """q scaled by 8: a peaked softmax, where a dropped or duplicated key tile is visible."""
+    B, H, Sq, Sk = 1, 2, 256, 700
+    r = np.random.default_rng(5)
+    q = synth.f32_to_bf16_bits((8 * r.standard_normal((B, H, Sq, D))).astype(np.float32))
+    k = synth.f32_to_bf16_bits(r.standard_normal((B, H, Sk, D)).astype(np.float32))
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, H, Sk, D)).astype(np.float32))
+    got = _run_dense(ka.ka_attn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, "bf16 peaked")
+
+
+def test_dense_bf16_workload_sampled():
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = synth.make_dense(wl)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 400, 11, edge=2, period=128)
+    r = assert_close(got[rows], oracle.attn(q, k, v, wl.scale, rows=rows), BF16_TOL, wl.key)
+    assert r["rel_rms"] < 1e-2
+
+
+def test_dense_bf16_deterministic():
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = (to_dev(x) for x in synth.make_dense(wl, B=1, H=3, Sq=1000, Sk=900))
+    a = ka.ka_attn_fwd(q, k, v)
+    b = ka.ka_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------------------------ cross
+
+def test_xattn_workload_full():
+    wl = W["sdxl_l2_cross_b2h20q1024k77"]
+    q, k, v = synth.make_dense(wl)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v, wl.scale)
+    assert_close(got, oracle.attn(q, k, v, wl.scale), BF16_TOL, wl.key)
+
+
+@pytest.mark.parametrize("Sk", [1, 13, 32, 33, 77, 96, 97, 128, 129, 200, 256])
+@pytest.mark.parametrize("Sq", [1, 50])
+def test_xattn_key_counts(Sq, Sk):
+    wl = W["sdxl_l2_cross_b2h20q1024k77"]
+    q, k, v = synth.make_dense(wl, seed_base=300 + Sk, B=1, H=2, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"xattn Sq={Sq} Sk={Sk}")
+
+
+def test_xattn_f32_routes_to_fp32_kernel():
+    wl = W["dense_f32_b1h2s256"]
+    q, k, v = synth.make_dense(wl, B=1, H=2, Sq=100, Sk=77)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), F32_TOL, "xattn f32")
+
+
+def test_xattn_matches_dense_kernel():
+    """The LDS-resident cross kernel and the flash kernel compute the same definition."""
+    wl = W["sdxl_l2_cross_b2h20q1024k77"]
+    q, k, v = (to_dev(x) for x in synth.make_dense(wl, B=1, H=4))
+    a = ka.ka_xattn_fwd(q, k, v).float()
+    b = ka.ka_attn_fwd(q, k, v).float()
+    torch.cuda.synchronize()
+    assert (a - b).abs().max().item() <= 2e-2
+
+
+# ------------------------------------------------------------------ differential
+
+def _run_diff(inputs, params, window, scale=0.125, base=10000.0):
+    q1, k1, q2, k2, v = (to_dev(x) for x in inputs)
+    a, g, b, lm = diff_params_dev(params)
+    o = nan_like(q1)
+    ka.ka_diffattn_fwd(q1, k1, q2, k2, v, a, g, b, lm, o=o, scale=scale, window=window, rope_base=base)
+    torch.cuda.synchronize()
+    return to_host_f64(o)
+
+
+def _oracle_diff(inputs, params, window, rows=None, scale=0.125, base=10000.0):
+    a, g, b, lm = params
+    return oracle.diffattn(*inputs, scale, window, a, g, b, base, lm, rows=rows)
+
+
+@pytest.mark.parametrize("S", [1, 2, 17, 18, 35, 36, 127, 128, 129, 391])
+def test_diff_band_lengths(S):
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl, seed_base=500 + S, S=S, H=2)
+    got = _run_diff(inputs, params, 17)
+    assert_close(got, _oracle_diff(inputs, params, 17), BF16_TOL, f"band S={S}")
+
+
+@pytest.mark.parametrize("window", [0, 1, 5, 16, 24, 25, 40, 41, 100, 298, 299, 1000, -1])
+def test_diff_windows(window):
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    S = 300
+    inputs, params = synth.make_diff(wl, seed_base=700 + max(window, 0), S=S, H=2, B=2)
+    got = _run_diff(inputs, params, window)
+    assert_close(got, _oracle_diff(inputs, params, window), BF16_TOL, f"window={window}")
+
+
+def test_diff_band_workload_sampled():
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl)
+    got = _run_diff(inputs, params, wl.window, wl.scale).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 1500, 13, edge=40, period=128)
+    assert_close(got[rows], _oracle_diff(inputs, params, wl.window, rows=rows, scale=wl.scale), BF16_TOL, wl.key)
+
+
+def test_diff_full_workload_sampled():
+    wl = W["sa3_dit_fulldiff_h16s1422"]
+    inputs, params = synth.make_diff(wl)
+    got = _run_diff(inputs, params, wl.window, wl.scale).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 3000, 17, edge=3, period=64)
+    assert_close(got[rows], _oracle_diff(inputs, params, wl.window, rows=rows, scale=wl.scale), BF16_TOL, wl.key)
+
+
+@pytest.mark.parametrize("window", [17, -1])
+def test_diff_branch_cancellation(window):
+    """Identical branches (same inputs, same parameter sets) and lambda = 1 give exactly zero."""
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    (q1, k1, _, _, v), (a, g, b, lm) = synth.make_diff(wl, seed_base=900, S=200, H=2)
+    g[2], g[3], b[2], b[3] = g[0], g[1], b[0], b[1]
+    got = _run_diff((q1, k1, q1, k1, v), (a, g, b, np.ones_like(lm)), window)
+    assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("window", [17, -1])
+def test_diff_constant_v(window):
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    (q1, k1, q2, k2, _), params = synth.make_diff(wl, seed_base=910, S=150, H=3)
+    c = synth.f32_to_bf16_bits(np.linspace(-2, 2, D).astype(np.float32))
+    v = np.ascontiguousarray(np.broadcast_to(c, q1.shape))
+    got = _run_diff((q1, k1, q2, k2, v), params, window)
+    want = (1.0 - params[3].astype(np.float64))[None, :, None, None] * oracle.widen(c)[None, None, None, :]
+    assert_close(got, np.broadcast_to(want, got.shape), 1e-2, f"constant V w={window}")
+
+
+def test_diff_deterministic():
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl, seed_base=920, S=1000, H=2)
+    a = _run_diff(inputs, params, 17)
+    b = _run_diff(inputs, params, 17)
+    assert np.array_equal(a, b)
