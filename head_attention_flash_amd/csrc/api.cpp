@@ -45,8 +45,9 @@ ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, 
   if (!std::isfinite(scale) || !(scale > 0.0f)) return KA_ERR_PARAM;
   const size_t e = dt == KA_F32 ? 4 : 2;
   if (!tensor_bytes(B, H, Sq, D, e, qbytes) || !tensor_bytes(B, H, Sk, D, e, kbytes)) return KA_ERR_SHAPE;
-  // the grid's y dimension carries B*H
+  // the grid's y dimension carries B*H; key tiles are addressed by 32-bit buffer offsets
   if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  if ((long long)Sk * D * (long long)e + 2LL * 64 * D * (long long)e > 0x7fffffffLL) return KA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KA_ERR_ALIGN;
   if (overlap(o, *qbytes, q, *qbytes) || overlap(o, *qbytes, k, *kbytes) || overlap(o, *qbytes, v, *kbytes))
     return KA_ERR_ALIAS;
@@ -141,7 +142,21 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   a.window = window < 0 ? -1 : window;
   a.c = scale * 1.4426950408889634f;
   const double two_pi = 6.283185307179586476925286766559;
-  for (int i = 0; i < 32; ++i) a.rev[i] = std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi;
+  // positions need ceil(log2 S) bits; rev_hi keeps 24 - that many significant bits so
+  // that p * rev_hi is exact in fp32, and rev_lo carries the rest
+  int pbits = 1;
+  while ((1 << pbits) < S) ++pbits;
+  a.split_angles = pbits <= 16;
+  for (int i = 0; i < 32; ++i) {
+    const double r = std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi;
+    a.rev[i] = r;
+    int ex = 0;
+    std::frexp(r, &ex);                                // r = m * 2^ex, 0.5 <= m < 1
+    const double q = std::ldexp(1.0, ex - (24 - pbits));
+    const double hi = std::round(r / q) * q;           // 24 - pbits significant bits
+    a.rev_hi[i] = (float)hi;
+    a.rev_lo[i] = (float)(r - hi);
+  }
   return hip_status(ka::launch_diffattn(a, stream));
 }
 

@@ -20,11 +20,12 @@
 // bf16 against the bf16 V; rotary angles are reduced in fp64.
 //
 // Kernels
-//   diff_band<NKB>     window <= 8*NKB-8: one workgroup per (b, h, 128-row
-//                      block).  The K1/K2/V rows the block can see (the rows plus
-//                      a halo of `window` on each side) are prepared once into LDS;
-//                      each 16-query tile then takes all its in-band keys in one
-//                      16*NKB-key slab: one exact softmax per branch, no rescale.
+//   diff_band<NKB>     window <= 8*NKB-8: one workgroup per strip of 64-row blocks
+//                      of one (b, h).  The K1/K2/V rows a block can see (its rows
+//                      plus a halo on each side) sit prepared in an LDS ring, each
+//                      prepared once per strip; each 16-query tile takes all its
+//                      in-band keys in one 16*NKB-key slab: one exact softmax per
+//                      branch, no rescale.
 //   diff_kprep         full (or wide-window) path, pass 1: DyT + rotation of K1 and
 //                      K2, once per (b, h) and key -- never once per query block
 //                      (V1 / Session 8: re-preparing K per query block was half the
@@ -40,19 +41,28 @@ constexpr int KPD = HD + 8;   // LDS pitch of prepared fp16 keys (elements)
 constexpr int VPD = HD + 16;  // LDS pitch of V (elements)
 
 struct SharedParams {
-  double rev[32];        // revolutions per position, pair i
-  float g[4][HD];        // DyT gamma per set (q1, k1, q2, k2)
-  float b[4][HD];        // DyT beta per set
+  double rev[32];        // revolutions per position, pair i (fp64 angle path)
+  float rev_hi[32];      // split fp32 angle path
+  float rev_lo[32];
+  float gpb[4][HD];      // DyT gamma + beta per set (q1, k1, q2, k2)
+  float m2g[4][HD];      // DyT -2 gamma per set
   float k2a[4];          // 2 log2(e) alpha per set
+  int split;
 };
 
 __device__ __forceinline__ void load_params(SharedParams& sp, const DiffArgs& a) {
   for (int i = threadIdx.x; i < 4 * HD; i += blockDim.x) {
-    sp.g[i / HD][i % HD] = a.gamma[i];
-    sp.b[i / HD][i % HD] = a.beta[i];
+    const float g = a.gamma[i], b = a.beta[i];
+    sp.gpb[i / HD][i % HD] = g + b;
+    sp.m2g[i / HD][i % HD] = -2.0f * g;
   }
-  if (threadIdx.x < 32) sp.rev[threadIdx.x] = a.rev[threadIdx.x];
+  if (threadIdx.x < 32) {
+    sp.rev[threadIdx.x] = a.rev[threadIdx.x];
+    sp.rev_hi[threadIdx.x] = a.rev_hi[threadIdx.x];
+    sp.rev_lo[threadIdx.x] = a.rev_lo[threadIdx.x];
+  }
   if (threadIdx.x < 4) sp.k2a[threadIdx.x] = 2.0f * LOG2E * a.alpha[threadIdx.x];
+  if (threadIdx.x == 0) sp.split = a.split_angles;
 }
 
 // DyT then rotation, for 8 rotary pairs (dims i0+e and i0+32+e) of two tensors
@@ -60,18 +70,23 @@ __device__ __forceinline__ void load_params(SharedParams& sp, const DiffArgs& a)
 __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int i0, int p, int ta,
                                             int tb, const SharedParams& sp) {
   const float ka = sp.k2a[ta], kb = sp.k2a[tb];
+  const float pf = (float)p;
+  const bool split = sp.split;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int i = i0 + e;
     float cs, sn;
-    rope_cs(p, sp.rev[i], cs, sn);
-    const float a0 = dyt(alo[e], ka, sp.g[ta][i], sp.b[ta][i]);
-    const float a1 = dyt(ahi[e], ka, sp.g[ta][i + 32], sp.b[ta][i + 32]);
+    if (split)
+      rope_cs_split(pf, sp.rev_hi[i], sp.rev_lo[i], cs, sn);
+    else
+      rope_cs_f64(p, sp.rev[i], cs, sn);
+    const float a0 = dyt(alo[e], ka, sp.gpb[ta][i], sp.m2g[ta][i]);
+    const float a1 = dyt(ahi[e], ka, sp.gpb[ta][i + 32], sp.m2g[ta][i + 32]);
     // explicit fused forms: every tensor rounds identically, whatever the compiler would contract
     alo[e] = __builtin_fmaf(a0, cs, -(a1 * sn));
     ahi[e] = __builtin_fmaf(a1, cs, a0 * sn);
-    const float b0 = dyt(blo[e], kb, sp.g[tb][i], sp.b[tb][i]);
-    const float b1 = dyt(bhi[e], kb, sp.g[tb][i + 32], sp.b[tb][i + 32]);
+    const float b0 = dyt(blo[e], kb, sp.gpb[tb][i], sp.m2g[tb][i]);
+    const float b1 = dyt(bhi[e], kb, sp.gpb[tb][i + 32], sp.m2g[tb][i + 32]);
     blo[e] = __builtin_fmaf(b0, cs, -(b1 * sn));
     bhi[e] = __builtin_fmaf(b1, cs, b0 * sn);
   }
@@ -80,7 +95,7 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
 __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
   f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (_Float16)f[e];
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)pin(f[e]);
   return r;
 }
 
@@ -95,136 +110,223 @@ __device__ __forceinline__ void load_pairs(const unsigned short* row, int i0, bo
   unpack_bf16x8(b, hi);
 }
 
-// One branch of a 16-query tile against a slab of 16*NKB keys in LDS, exact softmax
-// (all keys of the band are in the slab).  Returns O^T (un-normalised) and the sum.
-template <int NKB>
-__device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsigned short* Vs, int r0row,
-                                            const f16x8 (&Qf)[2], int jbase, int p, int window, int S, float c,
-                                            int col, int grp, f32x4 (&O)[4], float& l) {
+// ---------------------------------------------------------------- banded, strip-mined
+// One workgroup walks a strip of consecutive 64-row blocks of one (b, h).  The
+// prepared keys (DyT + rotation, fp16) and the values of every position the
+// current block can see -- its rows plus HALO on each side -- live in an LDS ring
+// of NR rows; moving to the next block adds 64 new rows and retires 64 old ones,
+// so each key is prepared once per strip, not once per block.  The raw rows the
+// next block adds, and its queries, are fetched into registers while the current
+// block computes.
+constexpr int BAND_BM = 64;  // query rows per block step: 4 waves x 16
+constexpr int BAND_NW = 4;
+constexpr int BAND_TARGET_WGS = 768;  // about three resident workgroups per CU
+#ifndef BAND_WPE
+#define BAND_WPE 3
+#endif
+
+// One thread's share of one new row: dims [8cc, 8cc+8) and [8cc+32, 8cc+40) of k1
+// and k2, and bytes [32cc, 32cc+32) of v.
+struct RowStage {
+  uint4 k1lo, k1hi, k2lo, k2hi, v0, v1;
+};
+
+__device__ __forceinline__ void stage_load(RowStage& st, const DiffArgs& a, size_t base, int j, bool ok, int cc) {
+  st.k1lo = st.k1hi = st.k2lo = st.k2hi = st.v0 = st.v1 = make_uint4(0, 0, 0, 0);
+  if (ok) {
+    const size_t off = base + (size_t)j * HD;
+    st.k1lo = ld16(a.k1 + off + 8 * cc);
+    st.k1hi = ld16(a.k1 + off + 32 + 8 * cc);
+    st.k2lo = ld16(a.k2 + off + 8 * cc);
+    st.k2hi = ld16(a.k2 + off + 32 + 8 * cc);
+    st.v0 = ld16(a.v + off + 16 * cc);
+    st.v1 = ld16(a.v + off + 16 * cc + 8);
+  }
+}
+
+__device__ __forceinline__ void stage_commit(const RowStage& st, unsigned short* K1s, unsigned short* K2s,
+                                             unsigned short* Vs, int slot, int j, bool ok, int cc,
+                                             const SharedParams& sp) {
+  float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
+  unpack_bf16x8(st.k1lo, k1lo);
+  unpack_bf16x8(st.k1hi, k1hi);
+  unpack_bf16x8(st.k2lo, k2lo);
+  unpack_bf16x8(st.k2hi, k2hi);
+  if (ok) prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);  // rows outside stay zero
+  st16(&K1s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1lo)));
+  st16(&K1s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1hi)));
+  st16(&K2s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2lo)));
+  st16(&K2s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2hi)));
+  st16(&Vs[slot * VPD + 16 * cc], st.v0);
+  st16(&Vs[slot * VPD + 16 * cc + 8], st.v1);
+}
+
+// One branch of a 16-query tile against the 16*NKB-key slab starting at ring slot
+// s0 (wrapping at NR); exact softmax over the slab; the row sum comes from an
+// all-ones MFMA over the same bf16 weights.
+template <int NKB, int NR>
+__device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsigned short* Vs, int s0,
+                                            const f16x8 (&Qf)[2], const bool (&ok)[NKB][4], float c, int col,
+                                            int grp, const bf16x8& ones, f32x4 (&O)[4], float& l) {
   f32x4 Sc[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    Sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(&Kh[(r0row + 16 * kb + col) * KPD + 32 * t + 8 * grp]);
-      Sc[kb] = mfma_f16(a, Qf[t], Sc[kb]);
-    }
+    int s = s0 + 16 * kb + col;
+    s = s >= NR ? s - NR : s;
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kh[s * KPD + 8 * grp]);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kh[s * KPD + 32 + 8 * grp]);
+    Sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    Sc[kb] = mfma_f16(a1, Qf[1], Sc[kb]);
   }
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int j = jbase + 16 * kb + 4 * grp + e;
-      const bool ok = (j >= p - window) && (j <= p + window) && (j >= 0) && (j < S);
-      Sc[kb][e] = ok ? Sc[kb][e] : -INFINITY;
+      Sc[kb][e] = ok[kb][e] ? Sc[kb][e] : -INFINITY;
       mx = fmaxf(mx, Sc[kb][e]);
     }
   const float mc = group4_max(mx) * c;
-  float ls = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pv = fast_exp2(__builtin_fmaf(Sc[kb][e], c, -mc));
-      Sc[kb][e] = pv;
-      ls += pv;
-    }
-  l = group4_sum(ls);
+    for (int e = 0; e < 4; ++e) Sc[kb][e] = fast_exp2(__builtin_fmaf(Sc[kb][e], c, -mc));
+  f32x4 L = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int db = 0; db < 4; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < NKB / 2; ++ks) {
     const bf16x8 P = pack_bf16(Sc[2 * ks], Sc[2 * ks + 1]);
-    const int vrow = r0row + 32 * ks + 4 * grp + (col >> 2);
+    int r = s0 + 32 * ks + 4 * grp + (col >> 2);
+    r = r >= NR ? r - NR : r;
+    int r16 = r + 16;
+    r16 = r16 >= NR ? r16 - NR : r16;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 a = cat_bf16(lds_read_tr16(&Vs[vrow * VPD + vcol]), lds_read_tr16(&Vs[(vrow + 16) * VPD + vcol]));
-      O[db] = mfma_bf16(a, P, O[db]);
+      const bf16x8 av = cat_bf16(lds_read_tr16(&Vs[r * VPD + vcol]), lds_read_tr16(&Vs[r16 * VPD + vcol]));
+      O[db] = mfma_bf16(av, P, O[db]);
     }
+    L = mfma_bf16(ones, P, L);
   }
+  l = L[0];
 }
 
-// ---------------------------------------------------------------- banded, one pass
-constexpr int BAND_BM = 128;  // query rows per workgroup
-constexpr int BAND_NW = 4;
-
-template <int NKB>
-__global__ __launch_bounds__(64 * BAND_NW) void diff_band(DiffArgs a) {
-  constexpr int HALO = 8 * NKB - 8;          // slab of query tile q0 starts at key q0 - HALO
-  constexpr int NR = BAND_BM + 2 * HALO;     // LDS rows: positions r0 - HALO .. r0 + BM + HALO - 1
+template <int NKB, int WPE>
+__global__ __launch_bounds__(64 * BAND_NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void diff_band(DiffArgs a, int nblk) {
+  constexpr int HALO = 8 * NKB - 8;       // slab of query tile q0 starts at key q0 - HALO
+  constexpr int NR = BAND_BM + 2 * HALO;  // ring rows
   __shared__ __align__(16) unsigned short K1s[NR * KPD];
   __shared__ __align__(16) unsigned short K2s[NR * KPD];
   __shared__ __align__(16) unsigned short Vs[NR * VPD];
   __shared__ SharedParams sp;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 15, grp = lane >> 4, cc = tid & 3;
   const int S = a.S, window = a.window;
   const size_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const int r0 = blockIdx.x * BAND_BM;
   const size_t base = bh * (size_t)S * HD;
+  const int strip0 = blockIdx.x * nblk * BAND_BM;
+  const int pos0 = strip0 - HALO;  // position held by ring slot 0
+  // every key any query of the strip can see; other rows are kept zero (and masked)
+  const int send = min(S, strip0 + nblk * BAND_BM);
+  const int jlo = max(0, strip0 - window), jhi = min(S - 1, send - 1 + window);
   load_params(sp, a);
   __syncthreads();
 
-  // ---- prepare the keys and values this block can see, once
-  const int jlo = max(0, r0 - window), jhi = min(S - 1, r0 + BAND_BM - 1 + window);
+  // fill the ring for the first block: positions pos0 .. pos0 + NR - 1
   for (int r = tid >> 2; r < NR; r += 64 * BAND_NW / 4) {
-    const int cc = tid & 3;
-    const int j = r0 - HALO + r;
-    const bool ok = (j >= jlo) && (j <= jhi);
-    float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
-    const ptrdiff_t jo = ok ? (ptrdiff_t)j * HD : 0;  // rows outside [jlo, jhi] are never read
-    load_pairs(a.k1 + base + jo, 8 * cc, ok, k1lo, k1hi);
-    load_pairs(a.k2 + base + jo, 8 * cc, ok, k2lo, k2hi);
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (ok) {
-      v0 = ld16(a.v + base + jo + 16 * cc);
-      v1 = ld16(a.v + base + jo + 16 * cc + 8);
-      prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);
-    }
-    st16(&K1s[r * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1lo)));
-    st16(&K1s[r * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1hi)));
-    st16(&K2s[r * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2lo)));
-    st16(&K2s[r * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2hi)));
-    st16(&Vs[r * VPD + 16 * cc], v0);
-    st16(&Vs[r * VPD + 16 * cc + 8], v1);
+    const int j = pos0 + r;
+    const bool ok = j >= jlo && j <= jhi;
+    RowStage st;
+    stage_load(st, a, base, j, ok, cc);
+    stage_commit(st, K1s, K2s, Vs, r, j, ok, cc, sp);
   }
+
+  // band mask by relative position: key j = q0 - HALO + 16kb + 4grp + e against
+  // query p = q0 + col, the same for every tile
+  bool band[NKB][4];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rel = -HALO + 16 * kb + 4 * grp + e - col;
+      band[kb][e] = rel >= -window && rel <= window;
+    }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float lam = a.lambda[h];
+
+  // queries of this wave for block 0
+  uint4 qs[4];
+  auto qload = [&](int r0) {
+    const int p = r0 + 16 * w + col;
+    qs[0] = qs[1] = qs[2] = qs[3] = make_uint4(0, 0, 0, 0);
+    if (p < S) {
+      const size_t off = base + (size_t)p * HD;
+      qs[0] = ld16(a.q1 + off + 8 * grp);
+      qs[1] = ld16(a.q1 + off + 32 + 8 * grp);
+      qs[2] = ld16(a.q2 + off + 8 * grp);
+      qs[3] = ld16(a.q2 + off + 32 + 8 * grp);
+    }
+  };
+  qload(strip0);
   __syncthreads();
 
-  const float lam = a.lambda[h];
-  // ---- 16-query tiles
-  for (int qb = w; qb < BAND_BM / 16; qb += BAND_NW) {
-    const int q0 = r0 + 16 * qb;
-    if (q0 >= S) break;
-    const int p = q0 + col;
-    const bool pok = p < S;
+  for (int b = 0; b < nblk; ++b) {
+    const int r0 = strip0 + b * BAND_BM;
+    if (r0 >= S) break;
+    const bool more = b + 1 < nblk && r0 + BAND_BM < S;
+    // prepared queries of this block
+    const int q0 = r0 + 16 * w, p = q0 + col;
     float q1lo[8], q1hi[8], q2lo[8], q2hi[8];
-    const size_t po = pok ? (size_t)p * HD : 0;
-    load_pairs(a.q1 + base + po, 8 * grp, pok, q1lo, q1hi);
-    load_pairs(a.q2 + base + po, 8 * grp, pok, q2lo, q2hi);
+    unpack_bf16x8(qs[0], q1lo);
+    unpack_bf16x8(qs[1], q1hi);
+    unpack_bf16x8(qs[2], q2lo);
+    unpack_bf16x8(qs[3], q2hi);
     prep_pairs2(q1lo, q1hi, q2lo, q2hi, 8 * grp, p, 0, 2, sp);
     const f16x8 Q1[2] = {to_f16x8(q1lo), to_f16x8(q1hi)};
     const f16x8 Q2[2] = {to_f16x8(q2lo), to_f16x8(q2hi)};
+    // fetch what the next block adds while this one computes
+    const int jn = r0 + BAND_BM + HALO + (tid >> 2);
+    const bool okn = more && jn >= jlo && jn <= jhi;
+    RowStage st;
+    stage_load(st, a, base, jn, okn, cc);
+    if (more) qload(r0 + BAND_BM);
 
+    const int jbase = q0 - HALO;
+    bool ok[NKB][4];
+    const bool edge = jbase < 0 || jbase + 16 * NKB > S;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jbase + 16 * kb + 4 * grp + e;
+        ok[kb][e] = band[kb][e] && (!edge || (j >= 0 && j < S));
+      }
+    const int s0 = (jbase - pos0) % NR;
     f32x4 O1[4], O2[4];
     float l1, l2;
-    const int jbase = q0 - HALO;  // key position of slab row 0; its LDS row is 16*qb
-    band_branch<NKB>(K1s, Vs, 16 * qb, Q1, jbase, p, window, S, a.c, col, grp, O1, l1);
-    band_branch<NKB>(K2s, Vs, 16 * qb, Q2, jbase, p, window, S, a.c, col, grp, O2, l2);
-    if (pok) {
+    band_branch<NKB, NR>(K1s, Vs, s0, Q1, ok, a.c, col, grp, ones, O1, l1);
+    band_branch<NKB, NR>(K2s, Vs, s0, Q2, ok, a.c, col, grp, ones, O2, l2);
+    if (p < S) {
       const float i1 = 1.0f / l1, i2 = lam / l2;
       unsigned short* orow = a.o + base + (size_t)p * HD;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = __fmul_rn(O1[db][e], i1) - __fmul_rn(O2[db][e], i2);
+        for (int e = 0; e < 4; ++e) r[e] = pin(O1[db][e] * i1) - pin(O2[db][e] * i2);
         st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
       }
+    }
+    if (more) {
+      __syncthreads();  // every wave is done with the rows about to be replaced
+      stage_commit(st, K1s, K2s, Vs, (jn - pos0) % NR, jn, okn, cc, sp);
+      __syncthreads();
     }
   }
 }
@@ -435,7 +537,7 @@ __global__ __launch_bounds__(64 * NW) void diff_flash(DiffArgs a) {
       for (int db = 0; db < 4; ++db) {
         f32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = __fmul_rn(O1[db][i][e], i1) - __fmul_rn(O2[db][i][e], i2);
+        for (int e = 0; e < 4; ++e) r[e] = pin(O1[db][i][e] * i1) - pin(O2[db][i][e] * i2);
         st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
       }
     }
@@ -455,11 +557,15 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
   if (a.window >= a.S - 1) a.window = -1;  // the band covers every key: full attention
   const int BH = a.B * a.H;
   if (use_band(a.S, a.window)) {
-    dim3 grid((a.S + BAND_BM - 1) / BAND_BM, BH);
+    // strips of nblk consecutive 64-row blocks, about BAND_TARGET_WGS workgroups in all
+    const int nb = (a.S + BAND_BM - 1) / BAND_BM;
+    int nblk = (int)(((long long)nb * BH + BAND_TARGET_WGS - 1) / BAND_TARGET_WGS);
+    nblk = nblk < 1 ? 1 : (nblk > 16 ? 16 : nblk);
+    dim3 grid((nb + nblk - 1) / nblk, BH);
     if (a.window <= 24)
-      hipLaunchKernelGGL(diff_band<4>, grid, dim3(64 * BAND_NW), 0, s, a);
+      hipLaunchKernelGGL((diff_band<4, BAND_WPE>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
     else
-      hipLaunchKernelGGL(diff_band<6>, grid, dim3(64 * BAND_NW), 0, s, a);
+      hipLaunchKernelGGL((diff_band<6, 2>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
     return hipGetLastError();
   }
   const size_t nrows = (size_t)BH * a.S;

@@ -52,6 +52,15 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pin a value in an fp32 register: the empty asm is opaque to the optimizer, so the
+// producing multiply cannot be contracted into a consumer (an FMA, or a mixed-
+// precision v_fma_mix that rounds once to fp16).  Used where two code paths must
+// round identically.
+__device__ __forceinline__ float pin(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i
 // receives slot e = element (i%4) of the 8 bytes addressed by source lane 4e + i/4.
 // With source lane s pointing at row r(s/4), column c0 + 4*(s%4) of a row-major
@@ -78,6 +87,22 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
+// Buffer resource over [base, base + bytes): raw buffer loads past `bytes` return
+// zero without touching memory, so tile loads need no per-lane branch.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_FLAGS = 0x00020000;  // dword 3 of a raw (untyped) buffer descriptor
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, RSRC_FLAGS);
+}
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, int byte_offset) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -100,27 +125,32 @@ __device__ __forceinline__ uint2 pack4_bf16_bits(float a, float b, float c, floa
   return __builtin_bit_cast(uint2, v);
 }
 
-// Parameters of the DyT + rotary preparation of one tensor (q1, k1, q2 or k2).
-struct PrepParams {
-  float k2a;          // 2 * log2(e) * alpha: tanh(alpha x) = 1 - 2 / (1 + 2^(k2a x))
-};
-
-// DyT: gamma * tanh(alpha * x) + beta, with tanh(y) = 1 - 2/(1 + e^{2y}).
-// Saturates correctly: e^{2y} -> inf gives 1, -> 0 gives -1.
-__device__ __forceinline__ float dyt(float x, float k2a, float gamma, float beta) {
-  float e = fast_exp2(k2a * x);
-  float r = __builtin_amdgcn_rcpf(1.0f + e);
-  float t = __builtin_fmaf(-2.0f, r, 1.0f);
-  return __builtin_fmaf(gamma, t, beta);
+// DyT: gamma * tanh(alpha x) + beta.  With tanh(y) = 1 - 2/(1 + e^{2y}) this is
+// (gamma + beta) - 2 gamma / (1 + e^{2 alpha x}): one exp, one reciprocal, one FMA,
+// given k2a = 2 log2(e) alpha, gpb = gamma + beta and m2g = -2 gamma.  It saturates
+// correctly: e^{2y} -> inf gives gamma + beta, e^{2y} -> 0 gives beta - gamma.
+__device__ __forceinline__ float dyt(float x, float k2a, float gpb, float m2g) {
+  const float e = fast_exp2(k2a * x);
+  return __builtin_fmaf(m2g, __builtin_amdgcn_rcpf(1.0f + e), gpb);
 }
 
-// Rotary angle of (position p, pair i) as cos/sin.  The angle in revolutions,
-// p * f_i / (2 pi), is formed and reduced to [-1/2, 1/2] in fp64 (an fp32 product
-// at p ~ 2e4 would be off by ~1e-3 rad); the hardware sin/cos take revolutions.
-__device__ __forceinline__ void rope_cs(int p, double rev_per_pos, float& c, float& s) {
+// Rotary angle of position p for one frequency, as cos/sin.  The angle in
+// revolutions, p * F (F = f / (2 pi)), is reduced to a small range before the
+// hardware sin/cos (which take revolutions): an fp32 product p * F at p ~ 2e4
+// would be off by ~1e-3 rad.
+//  split form (positions below 2^16): F = fhi + flo with fhi short enough that
+//    p * fhi is exact in fp32; u = (p fhi - rint(p fhi)) + p flo.
+//  fp64 form (longer sequences): u = p F - rint(p F) in double.
+__device__ __forceinline__ void rope_cs_split(float pf, float fhi, float flo, float& c, float& s) {
+  const float t = pf * fhi;
+  const float u = __builtin_fmaf(pf, flo, t - __builtin_rintf(t));
+  c = __builtin_amdgcn_cosf(u);
+  s = __builtin_amdgcn_sinf(u);
+}
+__device__ __forceinline__ void rope_cs_f64(int p, double rev_per_pos, float& c, float& s) {
   double t = (double)p * rev_per_pos;
   t -= __builtin_rint(t);
-  float f = (float)t;
+  const float f = (float)t;
   c = __builtin_amdgcn_cosf(f);
   s = __builtin_amdgcn_sinf(f);
 }

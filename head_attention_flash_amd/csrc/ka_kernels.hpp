@@ -31,6 +31,9 @@ struct DiffArgs {
   int window;              // >= 0: |i - j| <= window; < 0: all keys
   float c;                 // scale * log2(e)
   double rev[32];          // rope_base^(-2i/64) / (2 pi): revolutions per position of pair i
+  float rev_hi[32];        // rev split for fp32 angle reduction: rev_hi * p exact for p < 2^split_bits
+  float rev_lo[32];
+  int split_angles;        // 1: S <= 2^16, use rev_hi/rev_lo; 0: fp64 angles
 };
 
 // Largest window the one-pass band kernel takes; wider windows use the flash path.

@@ -164,6 +164,15 @@ def test_diff_band_lengths(S):
     assert_close(got, _oracle_diff(inputs, params, 17), BF16_TOL, f"band S={S}")
 
 
+@pytest.mark.parametrize("window", [17, 30])
+def test_diff_band_strips(window):
+    """Enough (b, h) slices that each workgroup walks several 64-row blocks through its key ring."""
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl, seed_base=800 + window, S=700, H=96, B=2)
+    got = _run_diff(inputs, params, window)
+    assert_close(got, _oracle_diff(inputs, params, window), BF16_TOL, f"band strips w={window}")
+
+
 @pytest.mark.parametrize("window", [0, 1, 5, 16, 24, 25, 40, 41, 100, 298, 299, 1000, -1])
 def test_diff_windows(window):
     wl = W["sa3_decoder_banddiff_h8s23086w17"]
