@@ -56,6 +56,43 @@ def time_launches(fn, nsets, steps, warmup, torch):
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
+def time_graph(fn, nsets, steps, warmup, torch):
+    """Like time_launches, with the `steps` launches captured once into a HIP graph and replayed,
+    so that host-side call overhead does not hide kernels shorter than it."""
+    for i in range(warmup):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                fn(i % nsets)
+    torch.cuda.synchronize()
+    g.replay()  # warm replay
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size (256 MiB read + 256 MiB written), launched once so a
+    counter run of this command also measures what FETCH_SIZE/WRITE_SIZE read for known bytes."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copy calibration {n} bytes")
+    del src, dst
+
+
 def source_digest(files):
     import hashlib
     h = hashlib.sha256()
@@ -99,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forms", default="cross,band,full", help="extra forms to time (comma list, or 'none')")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -113,6 +152,8 @@ def main():
         __graft_entry__.build()
     ka.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     # ---------------- headline: dense self-attention, SDXL level 1
     wl = synth.WORKLOADS["sdxl_l1_self_b2h10s4096"]
@@ -128,7 +169,7 @@ def main():
     sec = time_launches(step, 1, args.steps, args.warmup, torch)
     value = flops / sec / 1e12
     log(f"bench: dense {sec * 1e6:.1f} us/launch, {value:.1f} TFLOP/s")
-    traffic = traffic_for("attn_bf16_flash", 1)
+    traffic = traffic_for("attn_bf16_pipe", 1)
     result = {
         "metric": "attention TFLOP/s (% MFMA peak) dense; GB/s (% HBM peak) banded diff-attn",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -139,7 +180,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / sec / 1e12, 3),
                      "peak": acc.MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                      "frac": round(flops / sec / acc.MFMA_BF16_PEAK, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_flash", "flops_per_launch": flops},
+                     "kernel": "attn_bf16_pipe", "flops_per_launch": flops},
     }
     del q, k, v, o
 
@@ -152,8 +193,8 @@ def main():
         sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s)] for s in range(8)]
         outs = [torch.empty_like(s[0]) for s in sets]
         f, b = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk), acc.dense_bytes(wl.B, wl.H, wl.Sq, wl.Sk)
-        sec = time_launches(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
-                            args.warmup, torch)
+        sec = time_graph(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
+                         args.warmup, torch)
         forms["cross"] = {"workload": wl.key, "kernel": "xattn_bf16", "us": round(sec * 1e6, 3),
                           "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
                           "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
@@ -175,7 +216,7 @@ def main():
             ins, (a_, g_, b_, l_) = sets[i]
             ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window)
 
-        sec = time_launches(band, len(sets), args.steps, args.warmup, torch)
+        sec = time_graph(band, len(sets), args.steps, args.warmup, torch)
         forms["band_diff"] = {"workload": wl.key, "kernel": "diff_band", "us": round(sec * 1e6, 3),
                               "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
                               "TFLOP/s": round(f / sec / 1e12, 3), "bound": "hbm", "flops": f, "bytes": b,
@@ -193,9 +234,9 @@ def main():
         ws = torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
                          device="cuda")
         f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
-        sec = time_launches(lambda i: ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=o, scale=wl.scale,
-                                                         window=wl.window, workspace=ws),
-                            1, args.steps, args.warmup, torch)
+        sec = time_graph(lambda i: ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=o, scale=wl.scale,
+                                                      window=wl.window, workspace=ws),
+                         1, args.steps, args.warmup, torch)
         forms["full_diff"] = {"workload": wl.key, "kernel": "diff_kprep + diff_flash", "us": round(sec * 1e6, 3),
                               "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
                               "GB/s": round(b / sec / 1e9, 1), "bound": "mfma", "flops": f, "bytes": b}

@@ -225,3 +225,46 @@ def test_diff_deterministic():
     a = _run_diff(inputs, params, 17)
     b = _run_diff(inputs, params, 17)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_capture_replays_match_eager():
+    """All three entry points captured into one HIP graph; every replay, with eager work and
+    synchronisation in between, reproduces the eager results bit for bit."""
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = (to_dev(x) for x in synth.make_dense(wl, B=1, H=2, Sq=500, Sk=700))
+    xl = W["sdxl_l2_cross_b2h20q1024k77"]
+    xq, xk, xv = (to_dev(x) for x in synth.make_dense(xl, B=1, H=3, Sq=300))
+    dl = W["sa3_decoder_banddiff_h8s23086w17"]
+    ins, prm = synth.make_diff(dl, S=400, H=2)
+    ins = [to_dev(x) for x in ins]
+    prm = [to_dev(x) for x in prm]
+    ws = torch.empty(ka.ka_diffattn_workspace_bytes(1, 2, 400, 64, -1), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(q), torch.empty_like(xq), torch.empty_like(ins[0]), torch.empty_like(ins[0])]
+
+    def work():
+        ka.ka_attn_fwd(q, k, v, o=outs[0])
+        ka.ka_xattn_fwd(xq, xk, xv, o=outs[1])
+        ka.ka_diffattn_fwd(*ins, *prm, o=outs[2], window=17)
+        ka.ka_diffattn_fwd(*ins, *prm, o=outs[3], window=-1, workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        junk = (torch.randn(1 << 20, device="cuda") * 2).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del junk
+        for a, b in zip(outs, eager):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep} differs"
