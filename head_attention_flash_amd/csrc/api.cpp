@@ -45,7 +45,8 @@ ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, 
   if (!std::isfinite(scale) || !(scale > 0.0f)) return KA_ERR_PARAM;
   const size_t e = dt == KA_F32 ? 4 : 2;
   if (!tensor_bytes(B, H, Sq, D, e, qbytes) || !tensor_bytes(B, H, Sk, D, e, kbytes)) return KA_ERR_SHAPE;
-  // the grid's y dimension carries B*H; key tiles are addressed by 32-bit buffer offsets
+  // grids carry B*H (times the query blocks) in 32 bits; key tiles use 32-bit buffer offsets
+  if ((long long)B * H * ((Sq + 15) / 16) > 0x7fffffffLL) return KA_ERR_SHAPE;
   if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
   if ((long long)Sk * D * (long long)e + 2LL * 64 * D * (long long)e > 0x7fffffffLL) return KA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KA_ERR_ALIGN;

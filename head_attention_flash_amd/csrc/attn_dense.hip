@@ -108,11 +108,7 @@ constexpr int BN = 64;  // keys per tile
 //        multiplies P^T by an all-ones A operand, so the sum is taken over the
 //        same bf16-rounded weights that meet V, and no VALU add per score.
 //  LAZY: the running maximum is raised only when a tile's maximum exceeds it by
-//        more than 2^LAZY_LOG2 in weight; until then the weights are computed
-//        against the stale maximum (they stay below 2^LAZY_LOG2, far inside fp32
-//        and bf16 range) and O is not rescaled.  The final O / l is unchanged in
-//        exact arithmetic: both carry the same factor.
-constexpr float LAZY_LOG2 = 8.0f;
+//        more than 2^LAZY_LOG2 in weight (see ka_common.hpp).
 
 //  PRIO: raise the wave's issue priority while it issues matrix instructions, so
 //        that of two waves sharing a SIMD the one with MFMA work goes first and the
@@ -431,7 +427,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE > 0
 void attn_bf16_pipe(const unsigned short* __restrict__ q,
                                                           const unsigned short* __restrict__ k,
                                                           const unsigned short* __restrict__ v,
-                                                          unsigned short* __restrict__ o, int Sq, int Sk, float c) {
+                                                          unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                                                          int nbh) {
   __shared__ __align__(16) unsigned short Kb[2][BN * KP];
   __shared__ __align__(16) unsigned short Vb[2][BN * VP];
   constexpr int NT = 64 * NW;
@@ -439,8 +436,15 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const size_t bh = blockIdx.y;
-  const int q0 = (blockIdx.x * NW + w) * (16 * NQB);
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+  // Renumber them so that every XCD works through a contiguous run of (b, h, query
+  // block) items: the blocks of one (b, h) then share that XCD's L2 copy of K and V.
+  const int nqb = gridDim.x / nbh;  // query blocks per (b, h); the grid is nqb * nbh
+  const int nwg = gridDim.x, nwg8 = nwg & ~7;
+  int item = blockIdx.x;
+  if (item < nwg8) item = (item & 7) * (nwg8 >> 3) + (item >> 3);
+  const size_t bh = item / nqb;
+  const int q0 = ((item % nqb) * NW + w) * (16 * NQB);
   const unsigned short* qb = q + bh * (size_t)Sq * HD;
   const unsigned short* kbase = k + bh * (size_t)Sk * HD;
   const unsigned short* vbase = v + bh * (size_t)Sk * HD;
@@ -524,6 +528,433 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
     }
     pipe_pack<NQB>(Scur, R);
     pipe_rescale<NQB>(any, alpha, R);
+    if (NEXT && t + 2 < T) swrite(Kb[t & 1], KP, kr);
+    swrite(Vb[t & 1], VP, vr);
+    __syncthreads();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  if (T == 1) {
+    step(no{}, no{}, 0, Sa, Sb);
+  } else {
+    step(yes{}, no{}, 0, Sa, Sb);
+    int t = 1;
+    for (; t + 2 <= T - 1; t += 2) {
+      step(yes{}, yes{}, t, Sb, Sa);
+      step(yes{}, yes{}, t + 1, Sa, Sb);
+    }
+    if (t < T - 1) {
+      step(yes{}, yes{}, t, Sb, Sa);
+      step(no{}, yes{}, t + 1, Sa, Sb);
+    } else {
+      step(no{}, yes{}, t, Sb, Sa);
+    }
+  }
+  pipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
+
+  unsigned short* ob = o + bh * (size_t)Sq * HD;
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const float inv = 1.0f / R.L[i][0];
+    const int row = q0 + 16 * i + col;
+    if (row < Sq) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
+            pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 flash, phased
+// The pipelined loop with its phases pinned in order by scheduling barriers, so that
+// memory latency is covered by independent work instead of being waited on:
+//   1. global loads of the tiles two steps ahead (K) and one step ahead (V)
+//   2. every LDS read this step's MFMAs need (K(t+1) and V(t-1) fragments)
+//   3. the softmax of tile t on the VALU (the LDS reads land meanwhile)
+//   4. all MFMAs: S(t+1) = K(t+1) Q^T, O += V(t-1)^T P(t-1)^T, L += 1^T P(t-1)^T
+//   5. the rare rescale, then the staged tiles written to LDS; one barrier.
+template <int NQB, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_bf16_phased(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+                      const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                      int nbh) {
+  __shared__ __align__(16) unsigned short Kb[2][BN * KP];
+  __shared__ __align__(16) unsigned short Vb[2][BN * VP];
+  constexpr int NT = 64 * NW;
+  constexpr int CPT = (BN * 8 + NT - 1) / NT;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nqb = gridDim.x / nbh;
+  const int nwg = gridDim.x, nwg8 = nwg & ~7;
+  int item = blockIdx.x;
+  if (item < nwg8) item = (item & 7) * (nwg8 >> 3) + (item >> 3);
+  const size_t bh = item / nqb;
+  const int q0 = ((item % nqb) * NW + w) * (16 * NQB);
+  const unsigned short* qb = q + bh * (size_t)Sq * HD;
+  const unsigned short* kbase = k + bh * (size_t)Sk * HD;
+  const unsigned short* vbase = v + bh * (size_t)Sk * HD;
+
+  bf16x8 Qf[NQB][2];
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const int row = q0 + 16 * i + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
+      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  PipeRegs<NQB> R;
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    R.m[i] = -INFINITY;
+    R.L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) R.O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+  const int T = (Sk + BN - 1) / BN;
+  const rsrc_t krs = make_rsrc(kbase, Sk * HD * 2);
+  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
+  uint4 kr[CPT], vr[CPT];
+  auto gload = [&](const rsrc_t& src, int tile, uint4 (&r)[CPT]) {
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, tile * (BN * HD * 2) + (tid + ch * NT) * 16);
+  };
+  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch) {
+      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
+      if (CPT * NT == BN * 8 || idx < BN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
+    }
+  };
+
+  f32x4 Sa[4][NQB], Sb[4][NQB];
+  gload(krs, 0, kr);
+  swrite(Kb[0], KP, kr);
+  __syncthreads();
+  pipe_qk<NQB>(Kb[0], Qf, col, grp, Sa);
+  if (T > 1) {
+    gload(krs, 1, kr);
+    swrite(Kb[1], KP, kr);
+  }
+  __syncthreads();
+
+  auto step = [&](auto has_next, auto has_prev, int t, f32x4 (&Scur)[4][NQB], f32x4 (&Snext)[4][NQB]) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    constexpr bool PREV = decltype(has_prev)::value;
+    // 1. global loads for later steps
+    if (NEXT) gload(krs, t + 2, kr);
+    gload(vrs, t, vr);
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. LDS operand reads
+    bf16x8 kf[4][2], vf[2][4];
+    if (NEXT) {
+      const unsigned short* Kt = Kb[(t + 1) & 1];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          kf[kb4][tt] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb4 + col) * KP + 32 * tt + 8 * grp]);
+    }
+    if (PREV) {
+      const unsigned short* Vt = Vb[(t - 1) & 1];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int vrow = 32 * ks + 4 * grp + (col >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int vcol = 16 * db + 4 * (col & 3);
+          vf[ks][db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3+4. softmax of tile t interleaved with the matrix work: each MFMA is followed by
+    // one transcendental and two plain VALU instructions, which issue while it runs
+    float alpha[NQB];
+    const bool any = NEXT ? pipe_softmax<NQB, false>(Scur, t * BN, Sk, c, grp, R, alpha)
+                          : pipe_softmax<NQB, true>(Scur, t * BN, Sk, c, grp, R, alpha);
+    bf16x8 Pn[2][NQB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) {
+        Pn[ks][i] = pack_bf16(Scur[2 * ks][i], Scur[2 * ks + 1][i]);
+        asm volatile("" : "+v"(Pn[ks][i]));  // keep the weights in this region (no sinking)
+      }
+    if (NEXT) {
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int i = 0; i < NQB; ++i) {
+          Snext[kb4][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          Snext[kb4][i] = mfma_bf16(kf[kb4][1], Qf[i][1], Snext[kb4][i]);
+        }
+    }
+    if (PREV) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < NQB; ++i) R.O[db][i] = mfma_bf16(vf[ks][db], R.P[ks][i], R.O[db][i]);
+#pragma unroll
+        for (int i = 0; i < NQB; ++i) R.L[i] = mfma_bf16(ones, R.P[ks][i], R.L[i]);
+      }
+    }
+    {
+      constexpr int NM = (NEXT ? 8 * NQB : 0) + (PREV ? 10 * NQB : 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 8, 0);  // start the row-maximum chain
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_TRANS, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 5. rescale (rare), hand the weights to the next step, stage the loaded tiles
+    pipe_rescale<NQB>(any, alpha, R);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) R.P[ks][i] = Pn[ks][i];
+    if (NEXT && t + 2 < T) swrite(Kb[t & 1], KP, kr);
+    swrite(Vb[t & 1], VP, vr);
+    __syncthreads();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  if (T == 1) {
+    step(no{}, no{}, 0, Sa, Sb);
+  } else {
+    step(yes{}, no{}, 0, Sa, Sb);
+    int t = 1;
+    for (; t + 2 <= T - 1; t += 2) {
+      step(yes{}, yes{}, t, Sb, Sa);
+      step(yes{}, yes{}, t + 1, Sa, Sb);
+    }
+    if (t < T - 1) {
+      step(yes{}, yes{}, t, Sb, Sa);
+      step(no{}, yes{}, t + 1, Sa, Sb);
+    } else {
+      step(no{}, yes{}, t, Sb, Sa);
+    }
+  }
+  pipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
+
+  unsigned short* ob = o + bh * (size_t)Sq * HD;
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const float inv = 1.0f / R.L[i][0];
+    const int row = q0 + 16 * i + col;
+    if (row < Sq) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
+            pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 flash, hand-interleaved
+// One step of the pipelined loop with the instruction order fixed in the source:
+// each group below is fenced by a scheduling barrier, so the matrix instructions
+// of S(t+1) = K(t+1) Q^T and of P.V(t-1) alternate with the exponentials of the
+// softmax of tile t, which then issue while the MFMAs run.
+template <int NQB, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_bf16_ilv(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+                   const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                   int nbh) {
+  __shared__ __align__(16) unsigned short Kb[2][BN * KP];
+  __shared__ __align__(16) unsigned short Vb[2][BN * VP];
+  constexpr int NT = 64 * NW;
+  constexpr int CPT = (BN * 8 + NT - 1) / NT;
+  constexpr int NS = 16 * NQB;  // scores per lane per tile
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nqb = gridDim.x / nbh;
+  const int nwg = gridDim.x, nwg8 = nwg & ~7;
+  int item = blockIdx.x;
+  if (item < nwg8) item = (item & 7) * (nwg8 >> 3) + (item >> 3);
+  const size_t bh = item / nqb;
+  const int q0 = ((item % nqb) * NW + w) * (16 * NQB);
+  const unsigned short* qb = q + bh * (size_t)Sq * HD;
+  const unsigned short* kbase = k + bh * (size_t)Sk * HD;
+  const unsigned short* vbase = v + bh * (size_t)Sk * HD;
+
+  bf16x8 Qf[NQB][2];
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    const int row = q0 + 16 * i + col;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
+      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  PipeRegs<NQB> R;
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    R.m[i] = -INFINITY;
+    R.L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) R.O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+  const int T = (Sk + BN - 1) / BN;
+  const rsrc_t krs = make_rsrc(kbase, Sk * HD * 2);
+  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
+  uint4 kr[CPT], vr[CPT];
+  auto gload = [&](const rsrc_t& src, int tile, uint4 (&r)[CPT]) {
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, tile * (BN * HD * 2) + (tid + ch * NT) * 16);
+  };
+  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch) {
+      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
+      if (CPT * NT == BN * 8 || idx < BN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
+    }
+  };
+
+  f32x4 Sa[4][NQB], Sb[4][NQB];
+  gload(krs, 0, kr);
+  swrite(Kb[0], KP, kr);
+  __syncthreads();
+  pipe_qk<NQB>(Kb[0], Qf, col, grp, Sa);
+  if (T > 1) {
+    gload(krs, 1, kr);
+    swrite(Kb[1], KP, kr);
+  }
+  __syncthreads();
+
+  auto step = [&](auto has_next, auto has_prev, int t, f32x4 (&Scur)[4][NQB], f32x4 (&Snext)[4][NQB]) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    constexpr bool PREV = decltype(has_prev)::value;
+    if (NEXT) gload(krs, t + 2, kr);
+    gload(vrs, t, vr);
+    // LDS operand reads for this step's MFMAs
+    bf16x8 kf[4][2], vf[2][4];
+    if (NEXT) {
+      const unsigned short* Kt = Kb[(t + 1) & 1];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          kf[kb4][tt] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb4 + col) * KP + 32 * tt + 8 * grp]);
+    }
+    if (PREV) {
+      const unsigned short* Vt = Vb[(t - 1) & 1];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int vrow = 32 * ks + 4 * grp + (col >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int vcol = 16 * db + 4 * (col & 3);
+          vf[ks][db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // row maxima (the loads land meanwhile); ragged last tile masked first
+    if (!NEXT) {
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = t * BN + 16 * kb4 + 4 * grp + e < Sk;
+#pragma unroll
+          for (int i = 0; i < NQB; ++i) Scur[kb4][i][e] = ok ? Scur[kb4][i][e] : -INFINITY;
+        }
+    }
+    float alpha[NQB], mc[NQB];
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      float mx = Scur[0][i][0];
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Scur[kb4][i][e]);
+      mx = group4_max(mx);
+      const bool raise = (mx - R.m[i]) * c > LAZY_LOG2;
+      const float mnew = raise ? mx : R.m[i];
+      alpha[i] = fast_exp2((R.m[i] - mnew) * c);
+      R.m[i] = mnew;
+      mc[i] = mnew * c;
+      any = any || raise;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // weights element by element, each beside one MFMA
+    auto weight = [&](int idx) {
+      const int i = idx % NQB, kb4 = (idx / NQB) / 4, e = (idx / NQB) % 4;
+      float x = fast_exp2(__builtin_fmaf(Scur[kb4][i][e], c, -mc[i]));
+      asm volatile("" : "+v"(x));  // computed here, beside its MFMA, not sunk past the barrier
+      Scur[kb4][i][e] = x;
+    };
+    int wi = 0;
+    if (NEXT) {
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+        for (int i = 0; i < NQB; ++i) {
+          Snext[kb4][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          if (wi < NS) weight(wi++);
+          __builtin_amdgcn_sched_barrier(0);
+          Snext[kb4][i] = mfma_bf16(kf[kb4][1], Qf[i][1], Snext[kb4][i]);
+          if (wi < NS) weight(wi++);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (PREV) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < NQB; ++i) {
+            R.O[db][i] = mfma_bf16(vf[ks][db], R.P[ks][i], R.O[db][i]);
+            if (wi < NS) weight(wi++);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+        for (int i = 0; i < NQB; ++i) {
+          R.L[i] = mfma_bf16(ones, R.P[ks][i], R.L[i]);
+          if (wi < NS) weight(wi++);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+#pragma unroll
+    for (; wi < NS;) weight(wi++);  // tiles without enough matrix work
+    // bf16 weights for the next step's P.V
+    bf16x8 Pn[2][NQB];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) Pn[ks][i] = pack_bf16(Scur[2 * ks][i], Scur[2 * ks + 1][i]);
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_rescale<NQB>(any, alpha, R);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) R.P[ks][i] = Pn[ks][i];
     if (NEXT && t + 2 < T) swrite(Kb[t & 1], KP, kr);
     swrite(Vb[t & 1], VP, vr);
     __syncthreads();
@@ -697,8 +1128,9 @@ hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, co
   // on the SDXL level-1 workload (B=2, H=10, S=4096)
   constexpr int NQB = 1, NW = 4;
   const float c = scale * LOG2E;
-  dim3 grid((Sq + 16 * NQB * NW - 1) / (16 * NQB * NW), B * H);
-  hipLaunchKernelGGL((attn_bf16_pipe<NQB, NW, 0, 4>), grid, dim3(64 * NW), 0, s, q, k, v, o, Sq, Sk, c);
+  const int nqb = (Sq + 16 * NQB * NW - 1) / (16 * NQB * NW);
+  dim3 grid(nqb * B * H);  // one dimension: the kernel maps block -> (b, h, query block)
+  hipLaunchKernelGGL((attn_bf16_pipe<NQB, NW, 0, 4>), grid, dim3(64 * NW), 0, s, q, k, v, o, Sq, Sk, c, B * H);
   return hipGetLastError();
 }
 

@@ -30,8 +30,10 @@
 //                      K2, once per (b, h) and key -- never once per query block
 //                      (V1 / Session 8: re-preparing K per query block was half the
 //                      kernel's vector work) -- into the fp16 workspace.
-//   diff_flash<..>     pass 2: q prep in registers, then a two-branch flash loop
-//                      over 64-key tiles of the prepared keys and V.
+//   diff_flash<..>     pass 2: q prep in registers, then a pipelined two-branch
+//                      flash loop over 64-key tiles of the prepared keys and V.
+#include <type_traits>
+
 #include "ka_common.hpp"
 #include "ka_kernels.hpp"
 
@@ -353,28 +355,69 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   st16(w2 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2hi)));
 }
 
-// ---------------------------------------------------------------- full path, pass 2: two-branch flash
 constexpr int DBN = 64;  // keys per tile
 
+// ---------------------------------------------------------------- full path, pass 2: pipelined two-branch flash
+// The dense kernel's pipelined loop (S(t+1) and P.V(t-1) on the matrix core around the
+// softmax of tile t; buffer loads; row sums from an all-ones MFMA; lazily raised
+// maxima) carried over to two branches: prepared fp16 keys k1^, k2^ against the
+// prepared queries, one V shared by both P.V products (its fragments are read once).
+// BAND: keys outside |i - j| <= window are masked and whole tiles outside the band of
+// the workgroup are skipped (windows too wide for the one-pass band kernel).
 template <int NQB>
-__device__ __forceinline__ void flash_branch_tile(const unsigned short* Kt, const unsigned short* Vt,
-                                                  const f16x8 (&Qf)[NQB][2], int j0, int q0, int window, int S,
-                                                  float c, int col, int grp, float (&m)[NQB], float (&l)[NQB],
-                                                  f32x4 (&O)[4][NQB]) {
-  f32x4 Sc[4][NQB];
+struct DPipeRegs {
+  f32x4 O1[4][NQB], O2[4][NQB];
+  f32x4 L1[NQB], L2[NQB];
+  float m1[NQB], m2[NQB];
+  bf16x8 P1[2][NQB], P2[2][NQB];
+};
+
+template <int NQB>
+__device__ __forceinline__ void dpipe_qk(const unsigned short* Kt, const f16x8 (&Qf)[NQB][2], int col, int grp,
+                                         f32x4 (&S)[4][NQB]) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 8 * grp]);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 32 + 8 * grp]);
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) Sc[kb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const f16x8 a = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 32 * t + 8 * grp]);
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) Sc[kb][i] = mfma_f16(a, Qf[i][t], Sc[kb][i]);
+    for (int i = 0; i < NQB; ++i) {
+      S[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      S[kb][i] = mfma_f16(a1, Qf[i][1], S[kb][i]);
     }
   }
-  const bool need_mask = (j0 + DBN > S) || (window >= 0);
-  if (need_mask) {
+}
+
+template <int NQB>
+__device__ __forceinline__ void dpipe_pv(const unsigned short* Vt, const bf16x8& ones, int col, int grp,
+                                         DPipeRegs<NQB>& R) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int vrow = 32 * ks + 4 * grp + (col >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int vcol = 16 * db + 4 * (col & 3);
+      const bf16x8 av = cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) {
+        R.O1[db][i] = mfma_bf16(av, R.P1[ks][i], R.O1[db][i]);
+        R.O2[db][i] = mfma_bf16(av, R.P2[ks][i], R.O2[db][i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      R.L1[i] = mfma_bf16(ones, R.P1[ks][i], R.L1[i]);
+      R.L2[i] = mfma_bf16(ones, R.P2[ks][i], R.L2[i]);
+    }
+  }
+}
+
+// Softmax of one branch's tile against its lazily raised maxima; packs bf16 weights into
+// P and returns whether any maximum was raised (alpha = rescale factors).
+template <int NQB, bool MASK, bool BAND>
+__device__ __forceinline__ bool dpipe_softmax(f32x4 (&S)[4][NQB], int j0, int Slen, int window, int q0, float c,
+                                              int col, int grp, float (&m)[NQB], float (&alpha)[NQB],
+                                              bf16x8 (&P)[2][NQB]) {
+  if (MASK || BAND) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -383,63 +426,49 @@ __device__ __forceinline__ void flash_branch_tile(const unsigned short* Kt, cons
 #pragma unroll
         for (int i = 0; i < NQB; ++i) {
           const int p = q0 + 16 * i + col;
-          const bool ok = (j < S) && (window < 0 || (j >= p - window && j <= p + window));
-          Sc[kb][i][e] = ok ? Sc[kb][i][e] : -INFINITY;
+          const bool ok = (!MASK || j < Slen) && (!BAND || (j >= p - window && j <= p + window));
+          S[kb][i][e] = ok ? S[kb][i][e] : -INFINITY;
         }
       }
   }
+  bool any = false;
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    float mx = -INFINITY;
+    float mx = S[0][i][0];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Sc[kb][i][e]);
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb][i][e]);
     mx = group4_max(mx);
-    const float mnew = fmaxf(m[i], mx);
-    // a row that has seen no key yet (possible under a band) keeps m = -inf, l = 0, O = 0
-    const bool none = mnew == -INFINITY;
-    const float alpha = none ? 1.0f : fast_exp2((m[i] - mnew) * c);
-    const float mc = none ? 0.0f : mnew * c;
+    const bool raise = (mx - m[i]) * c > LAZY_LOG2;  // false for a row that has seen no key
+    const float mnew = raise ? mx : m[i];
+    alpha[i] = raise ? fast_exp2((m[i] - mnew) * c) : 1.0f;
     m[i] = mnew;
-    float ls = 0.0f;
+    any = any || raise;
+    const float mc = (BAND && mnew == -INFINITY) ? 0.0f : mnew * c;  // no key yet: all weights 0
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pv = fast_exp2(__builtin_fmaf(Sc[kb][i][e], c, -mc));
-        Sc[kb][i][e] = pv;
-        ls += pv;
-      }
-    l[i] = __builtin_fmaf(l[i], alpha, ls);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
+      for (int e = 0; e < 4; ++e) S[kb][i][e] = fast_exp2(__builtin_fmaf(S[kb][i][e], c, -mc));
   }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 P[NQB];
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) P[i] = pack_bf16(Sc[2 * ks][i], Sc[2 * ks + 1][i]);
-    const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 av = cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) O[db][i] = mfma_bf16(av, P[i], O[db][i]);
+    for (int i = 0; i < NQB; ++i) {
+      P[ks][i] = pack_bf16(S[2 * ks][i], S[2 * ks + 1][i]);
+      asm volatile("" : "+v"(P[ks][i]));  // materialise here, not past the rescale branch
     }
-  }
+  return any;
 }
 
-template <int NQB, int NW>
-__global__ __launch_bounds__(64 * NW) void diff_flash(DiffArgs a) {
-  __shared__ __align__(16) unsigned short K1s[2][DBN * KPD];
-  __shared__ __align__(16) unsigned short K2s[2][DBN * KPD];
-  __shared__ __align__(16) unsigned short Vs[2][DBN * VPD];
+template <int NQB, int NW, bool BAND>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void diff_flash(DiffArgs a) {
+  __shared__ __align__(16) unsigned short K1b[2][DBN * KPD];
+  __shared__ __align__(16) unsigned short K2b[2][DBN * KPD];
+  __shared__ __align__(16) unsigned short Vb[2][DBN * VPD];
   __shared__ SharedParams sp;
   constexpr int NT = 64 * NW;
-  constexpr int CPT = DBN * 8 / NT;
-  static_assert(CPT * NT == DBN * 8, "tile must split evenly over the block");
+  constexpr int CPT = (DBN * 8 + NT - 1) / NT;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -450,12 +479,11 @@ __global__ __launch_bounds__(64 * NW) void diff_flash(DiffArgs a) {
   const size_t nrows = (size_t)a.B * a.H * S;
   const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
   const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
-  const unsigned short* vb = a.v + base;
   load_params(sp, a);
   __syncthreads();
 
-  const int qblk0 = blockIdx.x * NW * 16 * NQB;  // first query of the workgroup
-  const int q0 = qblk0 + w * 16 * NQB;           // first query of this wave
+  const int qblk0 = blockIdx.x * NW * 16 * NQB;
+  const int q0 = qblk0 + w * 16 * NQB;
   f16x8 Q1[NQB][2], Q2[NQB][2];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
@@ -470,74 +498,136 @@ __global__ __launch_bounds__(64 * NW) void diff_flash(DiffArgs a) {
     Q2[i][0] = to_f16x8(q2lo);
     Q2[i][1] = to_f16x8(q2hi);
   }
+  DPipeRegs<NQB> R;
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    R.m1[i] = R.m2[i] = -INFINITY;
+    R.L1[i] = R.L2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) R.O1[db][i] = R.O2[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  // key tiles this workgroup can see
+  // key tiles this workgroup sees: all, or those touching its band
   int t_lo = 0, t_hi = (S - 1) / DBN;
-  if (window >= 0) {
+  if (BAND) {
     const int qlast = min(S - 1, qblk0 + NW * 16 * NQB - 1);
     t_lo = max(0, qblk0 - window) / DBN;
     t_hi = min(S - 1, qlast + window) / DBN;
   }
-
-  f32x4 O1[4][NQB], O2[4][NQB];
-  float m1[NQB], l1[NQB], m2[NQB], l2[NQB];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    m1[i] = m2[i] = -INFINITY;
-    l1[i] = l2[i] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) O1[db][i] = O2[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
+  const int T = t_hi - t_lo + 1;
+  const int rbytes = S * HD * 2;
+  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(a.v + base, rbytes);
   uint4 r1[CPT], r2[CPT], rv[CPT];
-  auto gload = [&](int tile) {
+  auto gload = [&](const rsrc_t& src, int u, uint4 (&r)[CPT]) {
+#pragma unroll
+    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, (t_lo + u) * (DBN * HD * 2) + (tid + ch * NT) * 16);
+  };
+  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
 #pragma unroll
     for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, r = idx >> 3, cc = idx & 7;
-      const int j = tile * DBN + r;
-      r1[ch] = r2[ch] = rv[ch] = make_uint4(0, 0, 0, 0);
-      if (j < S) {
-        r1[ch] = ld16(k1h + (size_t)j * HD + cc * 8);
-        r2[ch] = ld16(k2h + (size_t)j * HD + cc * 8);
-        rv[ch] = ld16(vb + (size_t)j * HD + cc * 8);
+      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
+      if (CPT * NT == DBN * 8 || idx < DBN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
+    }
+  };
+
+  f32x4 S1a[4][NQB], S1b[4][NQB], S2a[4][NQB], S2b[4][NQB];
+  gload(k1rs, 0, r1);
+  gload(k2rs, 0, r2);
+  swrite(K1b[0], KPD, r1);
+  swrite(K2b[0], KPD, r2);
+  __syncthreads();
+  dpipe_qk<NQB>(K1b[0], Q1, col, grp, S1a);
+  dpipe_qk<NQB>(K2b[0], Q2, col, grp, S2a);
+  if (T > 1) {
+    gload(k1rs, 1, r1);
+    gload(k2rs, 1, r2);
+    swrite(K1b[1], KPD, r1);
+    swrite(K2b[1], KPD, r2);
+  }
+  __syncthreads();
+
+  // step u (tile t_lo + u): S(u+1) and P.V(u-1) on the matrix core, softmax of tile u
+  auto step = [&](auto has_next, auto has_prev, int u, f32x4 (&S1c)[4][NQB], f32x4 (&S1n)[4][NQB],
+                  f32x4 (&S2c)[4][NQB], f32x4 (&S2n)[4][NQB]) {
+    constexpr bool NEXT = decltype(has_next)::value;
+    constexpr bool PREV = decltype(has_prev)::value;
+    if (NEXT) {
+      gload(k1rs, u + 2, r1);  // past the last tile: zeros, never written
+      gload(k2rs, u + 2, r2);
+    }
+    gload(vrs, u, rv);
+    if (NEXT) {
+      dpipe_qk<NQB>(K1b[(u + 1) & 1], Q1, col, grp, S1n);
+      dpipe_qk<NQB>(K2b[(u + 1) & 1], Q2, col, grp, S2n);
+    }
+    if (PREV) dpipe_pv<NQB>(Vb[(u - 1) & 1], ones, col, grp, R);
+    const int j0 = (t_lo + u) * DBN;
+    const bool tail = j0 + DBN > S;  // uniform
+    float al1[NQB], al2[NQB];
+    bool any;
+    if (tail) {
+      any = dpipe_softmax<NQB, true, BAND>(S1c, j0, S, window, q0, a.c, col, grp, R.m1, al1, R.P1);
+      any |= dpipe_softmax<NQB, true, BAND>(S2c, j0, S, window, q0, a.c, col, grp, R.m2, al2, R.P2);
+    } else {
+      any = dpipe_softmax<NQB, false, BAND>(S1c, j0, S, window, q0, a.c, col, grp, R.m1, al1, R.P1);
+      any |= dpipe_softmax<NQB, false, BAND>(S2c, j0, S, window, q0, a.c, col, grp, R.m2, al2, R.P2);
+    }
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          R.O1[db][i] *= al1[i];
+          R.O2[db][i] *= al2[i];
+        }
+        R.L1[i] *= al1[i];
+        R.L2[i] *= al2[i];
       }
     }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, r = idx >> 3, cc = idx & 7;
-      st16(&K1s[buf][r * KPD + cc * 8], r1[ch]);
-      st16(&K2s[buf][r * KPD + cc * 8], r2[ch]);
-      st16(&Vs[buf][r * VPD + cc * 8], rv[ch]);
+    if (NEXT && u + 2 < T) {
+      swrite(K1b[u & 1], KPD, r1);
+      swrite(K2b[u & 1], KPD, r2);
     }
-  };
-
-  gload(t_lo);
-  swrite(0);
-  __syncthreads();
-  for (int t = t_lo; t <= t_hi; ++t) {
-    const int buf = (t - t_lo) & 1;
-    if (t < t_hi) gload(t + 1);
-    flash_branch_tile<NQB>(K1s[buf], Vs[buf], Q1, t * DBN, q0, window, S, a.c, col, grp, m1, l1, O1);
-    flash_branch_tile<NQB>(K2s[buf], Vs[buf], Q2, t * DBN, q0, window, S, a.c, col, grp, m2, l2, O2);
-    if (t < t_hi) swrite(buf ^ 1);
+    swrite(Vb[u & 1], VPD, rv);
     __syncthreads();
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+
+  if (T == 1) {
+    step(no{}, no{}, 0, S1a, S1b, S2a, S2b);
+  } else {
+    step(yes{}, no{}, 0, S1a, S1b, S2a, S2b);
+    int u = 1;
+    for (; u + 2 <= T - 1; u += 2) {
+      step(yes{}, yes{}, u, S1b, S1a, S2b, S2a);
+      step(yes{}, yes{}, u + 1, S1a, S1b, S2a, S2b);
+    }
+    if (u < T - 1) {
+      step(yes{}, yes{}, u, S1b, S1a, S2b, S2a);
+      step(no{}, yes{}, u + 1, S1a, S1b, S2a, S2b);
+    } else {
+      step(no{}, yes{}, u, S1b, S1a, S2b, S2a);
+    }
   }
+  dpipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
 
   const float lam = a.lambda[h];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     const int p = q0 + 16 * i + col;
-    const float i1 = 1.0f / group4_sum(l1[i]);
-    const float i2 = lam / group4_sum(l2[i]);
+    const float i1 = 1.0f / R.L1[i][0];
+    const float i2 = lam / R.L2[i][0];
     if (p < S) {
       unsigned short* orow = a.o + base + (size_t)p * HD;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 r;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pin(O1[db][i][e] * i1) - pin(O2[db][i][e] * i2);
+        for (int e = 0; e < 4; ++e) r[e] = pin(R.O1[db][i][e] * i1) - pin(R.O2[db][i][e] * i2);
         st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
       }
     }
@@ -574,7 +664,10 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
   if (e != hipSuccess) return e;
   constexpr int NQB = 1, NW = 4;
   dim3 grid((a.S + 16 * NQB * NW - 1) / (16 * NQB * NW), BH);
-  hipLaunchKernelGGL((diff_flash<NQB, NW>), grid, dim3(64 * NW), 0, s, a);
+  if (a.window >= 0)
+    hipLaunchKernelGGL((diff_flash<NQB, NW, true>), grid, dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((diff_flash<NQB, NW, false>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 

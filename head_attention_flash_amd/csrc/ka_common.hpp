@@ -52,6 +52,13 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lazily raised running maximum of the online softmax: the reference maximum moves
+// only when a tile's maximum exceeds it by more than LAZY_LOG2 in the exp2 domain;
+// until then the weights are taken against the stale maximum (they stay below
+// 2^LAZY_LOG2, far inside fp32 and bf16 range) and O is not rescaled.  O / l is
+// unchanged in exact arithmetic: both carry the same factor.
+constexpr float LAZY_LOG2 = 8.0f;
+
 // Pin a value in an fp32 register: the empty asm is opaque to the optimizer, so the
 // producing multiply cannot be contracted into a consumer (an FMA, or a mixed-
 // precision v_fma_mix that rounds once to fp16).  Used where two code paths must
@@ -101,7 +108,8 @@ __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, int byte_offset) {
 }
 
 // Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100, SG_DS_WRITE = 0x200,
+              SG_TRANS = 0x400;
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
