@@ -169,7 +169,7 @@ def main():
     sec = time_launches(step, 1, args.steps, args.warmup, torch)
     value = flops / sec / 1e12
     log(f"bench: dense {sec * 1e6:.1f} us/launch, {value:.1f} TFLOP/s")
-    traffic = traffic_for("attn_bf16_pipe", 1)
+    traffic = traffic_for("attn_bf16_duo", 1)
     result = {
         "metric": "attention TFLOP/s (% MFMA peak) dense; GB/s (% HBM peak) banded diff-attn",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -180,7 +180,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / sec / 1e12, 3),
                      "peak": acc.MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                      "frac": round(flops / sec / acc.MFMA_BF16_PEAK, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_pipe", "flops_per_launch": flops},
+                     "kernel": "attn_bf16_duo", "flops_per_launch": flops},
     }
     del q, k, v, o
 

@@ -17,15 +17,19 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
+COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+
+
+# attention maxima are taken on finite scores or -inf: no IEEE NaN quieting around them
+PER_FILE = {"attn_dense.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_FILE.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in line and line.strip())

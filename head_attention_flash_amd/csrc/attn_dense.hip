@@ -9,17 +9,32 @@
 //
 // Kernels
 //   attn_f32_kernel        fp32 in/out, fp32 arithmetic; one thread per query.
-//   attn_bf16_flash<..>    bf16 in/out; S^T = K Q^T and O^T = V^T P^T on
-//                          v_mfma_f32_16x16x32_bf16, fp32 softmax; K/V tiles of 64
-//                          keys double-buffered in LDS; the 1/sum is applied once
-//                          per output row after P.V (the "divide after P.V" trim of
-//                          "401 -> 163 ms: Stable Audio 3 medium on one TPU v6e
-//                          chip", s4).
+//   attn_bf16_duo<NA, NB>  bf16 in/out, the large-grid path: 8 waves per block, two
+//                          per SIMD, each owning NA (waves 0-3) or NB (waves 4-7)
+//                          16-query blocks; S^T = K Q^T and O^T = V^T P^T on
+//                          v_mfma_f32_16x16x32_bf16 with fp32 softmax; 32-key K/V
+//                          tiles double-buffered in LDS; the matrix instructions of
+//                          one tile are interleaved by hand with the exponentials of
+//                          the previous one.  The 1/sum is applied once per output
+//                          row after P.V (the "divide after P.V" trim of "401 -> 163
+//                          ms: Stable Audio 3 medium on one TPU v6e chip", s4).
+//   attn_bf16_pipe<..>     the same arithmetic with 16 queries per wave and 64-key
+//                          tiles, four waves per SIMD: grids too small to fill the
+//                          chip with the 8-wave blocks.
 //   xattn_bf16<..>         cross-attention for short key sets: every key and value
 //                          of a (b, h) is loaded into LDS once and re-read by every
 //                          query tile ("SDXL as a requirements inventory" s5.7: hold
 //                          the re-read operand, stream Q/O); one exact softmax pass.
+//
+// Softmax bookkeeping shared by the bf16 kernels:
+//   * the row sum comes from the matrix core: one extra MFMA per 32 keys multiplies
+//     P^T by an all-ones A operand, so the sum is taken over the same bf16-rounded
+//     weights that meet V, with no VALU add per score;
+//   * the running maximum is raised lazily (LAZY_LOG2 in ka_common.hpp).
+// This file is compiled without NaN semantics (-fno-honor-nans): the maxima are
+// taken on finite scores or -inf, and IEEE NaN quieting would double their cost.
 #include <type_traits>
+#include <utility>
 
 #include "ka_common.hpp"
 #include "ka_kernels.hpp"
@@ -95,221 +110,16 @@ __global__ __launch_bounds__(F32_BQ) void attn_f32_kernel(const float* __restric
   }
 }
 
-// ---------------------------------------------------------------- bf16 flash
+// ---------------------------------------------------------------- bf16 constants
 // LDS pitches (in 16-bit elements): K rows are read as 16-byte A-operand chunks,
 // V rows through the transposed 8-byte read; both pitches keep a wave's reads on
 // distinct banks.
 constexpr int KP = HD + 8;
 constexpr int VP = HD + 16;
-constexpr int BN = 64;  // keys per tile
+constexpr int BN = 64;  // keys per tile of the 16-query kernel
 
-// Softmax bookkeeping choices:
-//  ONES: the row sum comes from the matrix core -- one extra MFMA per 32 keys
-//        multiplies P^T by an all-ones A operand, so the sum is taken over the
-//        same bf16-rounded weights that meet V, and no VALU add per score.
-//  LAZY: the running maximum is raised only when a tile's maximum exceeds it by
-//        more than 2^LAZY_LOG2 in weight (see ka_common.hpp).
-
-//  PRIO: raise the wave's issue priority while it issues matrix instructions, so
-//        that of two waves sharing a SIMD the one with MFMA work goes first and the
-//        other's softmax fills the gaps.
-template <int NQB, int NW, bool ONES, bool LAZY, bool PRIO = false>
-__global__ __launch_bounds__(64 * NW) void attn_bf16_flash(const unsigned short* __restrict__ q,
-                                                           const unsigned short* __restrict__ k,
-                                                           const unsigned short* __restrict__ v,
-                                                           unsigned short* __restrict__ o, int Sq, int Sk, float c) {
-  __shared__ __align__(16) unsigned short Ks[2][BN * KP];
-  __shared__ __align__(16) unsigned short Vs[2][BN * VP];
-  constexpr int NT = 64 * NW;
-  constexpr int CPT = (BN * 8 + NT - 1) / NT;  // 16-byte chunks per thread per tile and tensor
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const size_t bh = blockIdx.y;
-  const int q0 = (blockIdx.x * NW + w) * (16 * NQB);
-  const unsigned short* qb = q + bh * (size_t)Sq * HD;
-  const unsigned short* kb = k + bh * (size_t)Sk * HD;
-  const unsigned short* vb = v + bh * (size_t)Sk * HD;
-
-  // Q^T as B operands: lane owns query q0 + 16*i + col, dims 32*t + 8*grp .. +7.
-  bf16x8 Qf[NQB][2];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int row = q0 + 16 * i + col;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
-      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-
-  f32x4 O[4][NQB];
-  f32x4 L[NQB];  // ONES: row sums from the matrix core (all four entries equal)
-  float m[NQB], l[NQB];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.0f;
-    L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 4; ++db) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-
-  uint4 kr[CPT], vr[CPT];
-  auto gload = [&](int tile) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, r = idx >> 3, cc = idx & 7;
-      const int j = tile * BN + r;
-      kr[ch] = make_uint4(0, 0, 0, 0);
-      vr[ch] = make_uint4(0, 0, 0, 0);
-      if (idx < BN * 8 && j < Sk) {
-        kr[ch] = ld16(kb + (size_t)j * HD + cc * 8);
-        vr[ch] = ld16(vb + (size_t)j * HD + cc * 8);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, r = idx >> 3, cc = idx & 7;
-      if (idx < BN * 8) {
-        st16(&Ks[buf][r * KP + cc * 8], kr[ch]);
-        st16(&Vs[buf][r * VP + cc * 8], vr[ch]);
-      }
-    }
-  };
-
-  const int ntiles = (Sk + BN - 1) / BN;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const unsigned short* Kt = Ks[buf];
-    const unsigned short* Vt = Vs[buf];
-
-    // S^T (64 keys x 16*NQB queries), four 16-key blocks.
-    f32x4 S[4][NQB];
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) S[kb4][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb4 + col) * KP + 32 * tt + 8 * grp]);
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) S[kb4][i] = mfma_bf16(a, Qf[i][tt], S[kb4][i]);
-      }
-    }
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
-    if ((t + 1) * BN > Sk) {  // ragged last tile: absent keys never enter max or sum
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = t * BN + 16 * kb4 + 4 * grp + e < Sk;
-#pragma unroll
-          for (int i = 0; i < NQB; ++i) S[kb4][i][e] = ok ? S[kb4][i][e] : -INFINITY;
-        }
-    }
-
-    // online softmax in the exp2 domain: p = 2^(s*c - m*c), c = scale*log2(e)
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      float mx = S[0][i][0];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb4][i][e]);
-      mx = group4_max(mx);
-      float alpha = 1.0f;
-      if (LAZY) {
-        // raise the reference maximum only when weights would exceed 2^LAZY_LOG2
-        const bool raise = (mx - m[i]) * c > LAZY_LOG2;  // true on the first tile (m = -inf)
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-          const float mnew = raise ? mx : m[i];
-          alpha = fast_exp2((m[i] - mnew) * c);
-          m[i] = mnew;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
-          if (ONES) L[i] *= alpha;
-        }
-      } else {
-        const float mnew = fmaxf(m[i], mx);
-        alpha = fast_exp2((m[i] - mnew) * c);
-        m[i] = mnew;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
-        if (ONES) L[i] *= alpha;
-      }
-      const float mc = m[i] * c;
-      float ls = 0.0f;
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(S[kb4][i][e], c, -mc));
-          S[kb4][i][e] = p;
-          if (!ONES) ls += p;
-        }
-      if (!ONES) l[i] = __builtin_fmaf(l[i], alpha, ls);
-    }
-
-    // O^T += V^T P^T over two 32-key steps.
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 P[NQB];
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) P[i] = pack_bf16(S[2 * ks][i], S[2 * ks + 1][i]);
-      const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int vcol = 16 * db + 4 * (col & 3);
-        const i16x4 lo = lds_read_tr16(&Vt[vrow * VP + vcol]);
-        const i16x4 hi = lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]);
-        const bf16x8 a = cat_bf16(lo, hi);
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) O[db][i] = mfma_bf16(a, P[i], O[db][i]);
-      }
-      if (ONES) {
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) L[i] = mfma_bf16(ones, P[i], L[i]);
-      }
-    }
-
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
-
-    if (t + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: one division per output element row, after P.V
-  unsigned short* ob = o + bh * (size_t)Sq * HD;
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const float inv = 1.0f / (ONES ? L[i][0] : group4_sum(l[i]));
-    const int row = q0 + 16 * i + col;
-    if (row < Sq) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(O[db][i][0] * inv, O[db][i][1] * inv, O[db][i][2] * inv, O[db][i][3] * inv));
-    }
-  }
-}
-
-// ---------------------------------------------------------------- bf16 flash, software-pipelined
-// The same arithmetic as attn_bf16_flash<NQB, NW, true, true>, reordered so that
-// the matrix core and the vector unit work at the same time inside one wave:
+// ---------------------------------------------------------------- bf16, 16 queries per wave, software-pipelined
+// The matrix core and the vector unit work at the same time inside one wave:
 // while the softmax of key tile t runs on the VALU, the wave has already issued
 // the MFMAs of S(t+1) = K(t+1) Q^T and of O += V(t-1)^T P(t-1)^T, which do not
 // depend on it.  LDS holds K one tile ahead and V one tile behind:
@@ -567,35 +377,42 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
   }
 }
 
-// ---------------------------------------------------------------- bf16 flash, phased
-// The pipelined loop with its phases pinned in order by scheduling barriers, so that
-// memory latency is covered by independent work instead of being waited on:
-//   1. global loads of the tiles two steps ahead (K) and one step ahead (V)
-//   2. every LDS read this step's MFMAs need (K(t+1) and V(t-1) fragments)
-//   3. the softmax of tile t on the VALU (the LDS reads land meanwhile)
-//   4. all MFMAs: S(t+1) = K(t+1) Q^T, O += V(t-1)^T P(t-1)^T, L += 1^T P(t-1)^T
-//   5. the rare rescale, then the staged tiles written to LDS; one barrier.
-template <int NQB, int NW, int WPE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void attn_bf16_phased(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
-                      const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
-                      int nbh) {
-  __shared__ __align__(16) unsigned short Kb[2][BN * KP];
-  __shared__ __align__(16) unsigned short Vb[2][BN * VP];
-  constexpr int NT = 64 * NW;
-  constexpr int CPT = (BN * 8 + NT - 1) / NT;
+// ---------------------------------------------------------------- bf16, 8 waves per block
+// Block layout: 512 threads, two waves per SIMD.  Waves 0-3 own NA query blocks of
+// 16 queries each, waves 4-7 own NB, so one SIMD carries NA + NB blocks and a block
+// covers 64 (NA + NB) queries of one (b, h).  Keys stream in 32-key tiles through a
+// two-deep LDS ring; step t of a wave
+//   * issues the matrix work of S(t+1) = K(t+1) Q^T and of O += V(t-1)^T P(t-1)^T,
+//   * computes the weights of tile t on the vector unit, one weight (or one bf16
+//     pack) beside each MFMA, the instruction order fixed by scheduling barriers,
+//   * stores the staged K(t+2) / V(t) into the ring slots read last in step t-1,
+// then the block synchronises once.  Threads 0-255 stage K, 256-511 stage V, one
+// 16-byte chunk each per tile, loaded one step before it is stored.
+//
+// Lazy maximum with a vote: a lane compares the maximum of its 8 scores of a tile
+// with the threshold m + LAZY_LOG2 / c; only when some lane of the wave exceeds it
+// are the four-lane maxima taken and the reference maximum raised (the accumulator
+// rescaled after this step's P.V).  Other tiles cost one compare per block.
+constexpr int DBN = 32;  // keys per tile
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int nqb = gridDim.x / nbh;
-  const int nwg = gridDim.x, nwg8 = nwg & ~7;
-  int item = blockIdx.x;
-  if (item < nwg8) item = (item & 7) * (nwg8 >> 3) + (item >> 3);
-  const size_t bh = item / nqb;
-  const int q0 = ((item % nqb) * NW + w) * (16 * NQB);
-  const unsigned short* qb = q + bh * (size_t)Sq * HD;
-  const unsigned short* kbase = k + bh * (size_t)Sk * HD;
-  const unsigned short* vbase = v + bh * (size_t)Sk * HD;
+struct DuoLds {
+  unsigned short K[2][DBN * KP];
+  unsigned short V[2][DBN * VP];
+};
+
+template <int NQB>
+__device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __restrict__ qb, int Sq, int q0,
+                                         const unsigned short* kbase, const unsigned short* vbase, int Sk, float c,
+                                         unsigned short* __restrict__ ob, int tid) {
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const bool isK = tid < 256;
+  const int chunk = tid & 255, srow = chunk >> 3, scol = (chunk & 7) * 8;
+  // rows past Sk read as zero through the buffer resource
+  const rsrc_t srs = make_rsrc(isK ? kbase : vbase, Sk * HD * 2);
+  const int lead = isK ? 2 : 0;  // step t stores tile t + lead and loads tile t + lead + 1
+  unsigned short* sdst0 = isK ? &sm.K[0][srow * KP + scol] : &sm.V[0][srow * VP + scol];
+  unsigned short* sdst1 = isK ? &sm.K[1][srow * KP + scol] : &sm.V[1][srow * VP + scol];
+  auto ldt = [&](int tile) { return buf_ld16(srs, tile * (DBN * HD * 2) + chunk * 16); };
 
   bf16x8 Qf[NQB][2];
 #pragma unroll
@@ -608,390 +425,221 @@ void attn_bf16_phased(const unsigned short* __restrict__ q, const unsigned short
       Qf[i][t] = __builtin_bit_cast(bf16x8, u);
     }
   }
-  PipeRegs<NQB> R;
+  f32x4 O[4][NQB], L[NQB];
+  float mc[NQB], thr[NQB];  // reference maximum times c; raise threshold in score units
+  bf16x8 P[NQB];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    R.m[i] = -INFINITY;
-    R.L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mc[i] = -INFINITY;
+    thr[i] = -INFINITY;
+    L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < 4; ++db) R.O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < 4; ++db) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  const float lazy_s = LAZY_LOG2 / c, inv_c = 1.0f / c;
 
-  const int T = (Sk + BN - 1) / BN;
-  const rsrc_t krs = make_rsrc(kbase, Sk * HD * 2);
-  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
-  uint4 kr[CPT], vr[CPT];
-  auto gload = [&](const rsrc_t& src, int tile, uint4 (&r)[CPT]) {
+  const int T = (Sk + DBN - 1) / DBN;
+  uint4 st[2];
+  f32x4 Sa[2][NQB], Sb[2][NQB];
+  // prologue: K(0) -> K[0], S(0) = K(0) Q^T; K(1) -> K[1]; stage K(2) / V(0)
+  if (isK) st16(sdst0, ldt(0));
+  __syncthreads();
 #pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, tile * (BN * HD * 2) + (tid + ch * NT) * 16);
-  };
-  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
+  for (int kb = 0; kb < 2; ++kb) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sm.K[0][(16 * kb + col) * KP + 8 * grp]);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sm.K[0][(16 * kb + col) * KP + 32 + 8 * grp]);
 #pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
-      if (CPT * NT == BN * 8 || idx < BN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
+    for (int i = 0; i < NQB; ++i) {
+      Sa[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      Sa[kb][i] = mfma_bf16(a1, Qf[i][1], Sa[kb][i]);
     }
-  };
-
-  f32x4 Sa[4][NQB], Sb[4][NQB];
-  gload(krs, 0, kr);
-  swrite(Kb[0], KP, kr);
-  __syncthreads();
-  pipe_qk<NQB>(Kb[0], Qf, col, grp, Sa);
-  if (T > 1) {
-    gload(krs, 1, kr);
-    swrite(Kb[1], KP, kr);
   }
+  if (isK && T > 1) st16(sdst1, ldt(1));
+  st[0] = ldt(lead);
   __syncthreads();
 
-  auto step = [&](auto has_next, auto has_prev, int t, f32x4 (&Scur)[4][NQB], f32x4 (&Snext)[4][NQB]) {
+  auto step = [&](auto has_next, auto has_prev, auto parity, int t, f32x4 (&Sc)[2][NQB], f32x4 (&Sn)[2][NQB]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
-    // 1. global loads for later steps
-    if (NEXT) gload(krs, t + 2, kr);
-    gload(vrs, t, vr);
-    __builtin_amdgcn_sched_barrier(0);
-    // 2. LDS operand reads
-    bf16x8 kf[4][2], vf[2][4];
+    constexpr int PAR = decltype(parity)::value;  // t & 1
+    st[PAR ^ 1] = ldt(t + lead + 1);  // past the last tile: zeros, never stored
+    bf16x8 kf[2][2], vf[4];
     if (NEXT) {
-      const unsigned short* Kt = Kb[(t + 1) & 1];
+      const unsigned short* Kt = sm.K[PAR ^ 1];
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          kf[kb4][tt] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb4 + col) * KP + 32 * tt + 8 * grp]);
+        for (int h = 0; h < 2; ++h)
+          kf[kb][h] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb + col) * KP + 32 * h + 8 * grp]);
     }
     if (PREV) {
-      const unsigned short* Vt = Vb[(t - 1) & 1];
+      // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
+      // (keys 4*grp + e of the first 16-key half, then of the second)
+      const unsigned short* Vt = sm.V[PAR ^ 1];
+      const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int vcol = 16 * db + 4 * (col & 3);
-          vf[ks][db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
-        }
+      for (int db = 0; db < 4; ++db) {
+        const int vcol = 16 * db + 4 * (col & 3);
+        vf[db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // 3+4. softmax of tile t interleaved with the matrix work: each MFMA is followed by
-    // one transcendental and two plain VALU instructions, which issue while it runs
-    float alpha[NQB];
-    const bool any = NEXT ? pipe_softmax<NQB, false>(Scur, t * BN, Sk, c, grp, R, alpha)
-                          : pipe_softmax<NQB, true>(Scur, t * BN, Sk, c, grp, R, alpha);
-    bf16x8 Pn[2][NQB];
+    if (!NEXT) {  // last tile: keys past Sk take no weight
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = t * DBN + 16 * kb + 4 * grp + e < Sk;
+#pragma unroll
+          for (int i = 0; i < NQB; ++i) Sc[kb][i][e] = ok ? Sc[kb][i][e] : -INFINITY;
+        }
+    }
+    float lmx[NQB];
+    bool exceed = false;
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      lmx[i] = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
+                     fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
+      exceed = exceed || lmx[i] > thr[i];
+    }
+    float alpha[NQB];
+    const bool raised = __builtin_amdgcn_ballot_w64(exceed) != 0;
+    if (raised) {  // true on the first tile (threshold -inf)
 #pragma unroll
       for (int i = 0; i < NQB; ++i) {
-        Pn[ks][i] = pack_bf16(Scur[2 * ks][i], Scur[2 * ks + 1][i]);
-        asm volatile("" : "+v"(Pn[ks][i]));  // keep the weights in this region (no sinking)
-      }
-    if (NEXT) {
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-          Snext[kb4][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          Snext[kb4][i] = mfma_bf16(kf[kb4][1], Qf[i][1], Snext[kb4][i]);
-        }
-    }
-    if (PREV) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < NQB; ++i) R.O[db][i] = mfma_bf16(vf[ks][db], R.P[ks][i], R.O[db][i]);
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) R.L[i] = mfma_bf16(ones, R.P[ks][i], R.L[i]);
-      }
-    }
-    {
-      constexpr int NM = (NEXT ? 8 * NQB : 0) + (PREV ? 10 * NQB : 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 8, 0);  // start the row-maximum chain
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_TRANS, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+        const float mcn = fmaxf(mc[i], group4_max(lmx[i]) * c);
+        alpha[i] = fast_exp2(mc[i] - mcn);  // 0 on the first tile
+        mc[i] = mcn;
+        thr[i] = __builtin_fmaf(mcn, inv_c, lazy_s);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 5. rescale (rare), hand the weights to the next step, stage the loaded tiles
-    pipe_rescale<NQB>(any, alpha, R);
+    constexpr int NQK = NEXT ? 4 * NQB : 0;
+    constexpr int NM = NQK + (PREV ? 5 * NQB : 0);
+    auto mfma_at = [&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      if constexpr (j < NQK) {
+        constexpr int i = j / 4, kb = (j / 2) % 2, h = j % 2;
+        if constexpr (h == 0)
+          Sn[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        else
+          Sn[kb][i] = mfma_bf16(kf[kb][1], Qf[i][1], Sn[kb][i]);
+      } else if constexpr (j < NM) {
+        constexpr int jp = j - NQK, i = jp / 5, db = jp % 5;
+        if constexpr (db < 4)
+          O[db][i] = mfma_bf16(vf[db], P[i], O[db][i]);
+        else
+          L[i] = mfma_bf16(ones, P[i], L[i]);
+      }
+    };
+    bf16x8 Pn[NQB];
+    auto valu_at = [&](auto ss) {
+      constexpr int s = decltype(ss)::value;
+      constexpr int i = s / 9, e = s % 9;
+      if constexpr (i < NQB) {
+        if constexpr (e < 8) {
+          float x = fast_exp2(__builtin_fmaf(Sc[e >> 2][i][e & 3], c, -mc[i]));
+          asm volatile("" : "+v"(x));  // computed in its slot, not sunk past the next barrier
+          Sc[e >> 2][i][e & 3] = x;
+        } else {
+          Pn[i] = pack_bf16(Sc[0][i], Sc[1][i]);
+          asm volatile("" : "+v"(Pn[i]));
+        }
+      }
+    };
+    // slot s: MFMA s, then vector work s (8 weights and one pack per query block)
+    constexpr int NSLOT = (NM > 9 * NQB) ? NM : 9 * NQB;
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      ([&] {
+        mfma_at(std::integral_constant<int, S>{});
+        valu_at(std::integral_constant<int, S>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }(), ...);
+    }(std::make_integer_sequence<int, NSLOT>{});
+    if (raised) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int i = 0; i < NQB; ++i) {
 #pragma unroll
-      for (int i = 0; i < NQB; ++i) R.P[ks][i] = Pn[ks][i];
-    if (NEXT && t + 2 < T) swrite(Kb[t & 1], KP, kr);
-    swrite(Vb[t & 1], VP, vr);
+        for (int db = 0; db < 4; ++db) O[db][i] *= alpha[i];
+        L[i] *= alpha[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) P[i] = Pn[i];
+    if (t + lead < T) st16(PAR ? sdst1 : sdst0, st[PAR]);
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
-
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   if (T == 1) {
-    step(no{}, no{}, 0, Sa, Sb);
+    step(no{}, no{}, P0{}, 0, Sa, Sb);
   } else {
-    step(yes{}, no{}, 0, Sa, Sb);
+    step(yes{}, no{}, P0{}, 0, Sa, Sb);
     int t = 1;
     for (; t + 2 <= T - 1; t += 2) {
-      step(yes{}, yes{}, t, Sb, Sa);
-      step(yes{}, yes{}, t + 1, Sa, Sb);
+      step(yes{}, yes{}, P1{}, t, Sb, Sa);
+      step(yes{}, yes{}, P0{}, t + 1, Sa, Sb);
     }
     if (t < T - 1) {
-      step(yes{}, yes{}, t, Sb, Sa);
-      step(no{}, yes{}, t + 1, Sa, Sb);
+      step(yes{}, yes{}, P1{}, t, Sb, Sa);
+      step(no{}, yes{}, P0{}, t + 1, Sa, Sb);
     } else {
-      step(no{}, yes{}, t, Sb, Sa);
+      step(no{}, yes{}, P1{}, t, Sb, Sa);
     }
   }
-  pipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
-
-  unsigned short* ob = o + bh * (size_t)Sq * HD;
+  {  // P.V of the last tile
+    const unsigned short* Vt = sm.V[(T - 1) & 1];
+    const int vrow = 4 * grp + (col >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int vcol = 16 * db + 4 * (col & 3);
+      const bf16x8 a = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) O[db][i] = mfma_bf16(a, P[i], O[db][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) L[i] = mfma_bf16(ones, P[i], L[i]);
+  }
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    const float inv = 1.0f / R.L[i][0];
+    const float inv = 1.0f / L[i][0];
     const int row = q0 + 16 * i + col;
     if (row < Sq) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv));
+            pack4_bf16_bits(O[db][i][0] * inv, O[db][i][1] * inv, O[db][i][2] * inv, O[db][i][3] * inv));
     }
   }
 }
 
-// ---------------------------------------------------------------- bf16 flash, hand-interleaved
-// One step of the pipelined loop with the instruction order fixed in the source:
-// each group below is fenced by a scheduling barrier, so the matrix instructions
-// of S(t+1) = K(t+1) Q^T and of P.V(t-1) alternate with the exponentials of the
-// softmax of tile t, which then issue while the MFMAs run.
-template <int NQB, int NW, int WPE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void attn_bf16_ilv(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+// grid: nqb * nbh blocks of 512 threads, block -> (b, h, query block) with the
+// XCD-aware renumbering of attn_bf16_pipe
+template <int NA, int NB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_duo(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
                    const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
                    int nbh) {
-  __shared__ __align__(16) unsigned short Kb[2][BN * KP];
-  __shared__ __align__(16) unsigned short Vb[2][BN * VP];
-  constexpr int NT = 64 * NW;
-  constexpr int CPT = (BN * 8 + NT - 1) / NT;
-  constexpr int NS = 16 * NQB;  // scores per lane per tile
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  __shared__ __align__(16) DuoLds sm;
+  const int tid = threadIdx.x, w = tid >> 6;
   const int nqb = gridDim.x / nbh;
   const int nwg = gridDim.x, nwg8 = nwg & ~7;
   int item = blockIdx.x;
   if (item < nwg8) item = (item & 7) * (nwg8 >> 3) + (item >> 3);
   const size_t bh = item / nqb;
-  const int q0 = ((item % nqb) * NW + w) * (16 * NQB);
+  const int base = (item % nqb) * (64 * (NA + NB));
   const unsigned short* qb = q + bh * (size_t)Sq * HD;
-  const unsigned short* kbase = k + bh * (size_t)Sk * HD;
-  const unsigned short* vbase = v + bh * (size_t)Sk * HD;
-
-  bf16x8 Qf[NQB][2];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int row = q0 + 16 * i + col;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
-      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-  PipeRegs<NQB> R;
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    R.m[i] = -INFINITY;
-    R.L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 4; ++db) R.O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-
-  const int T = (Sk + BN - 1) / BN;
-  const rsrc_t krs = make_rsrc(kbase, Sk * HD * 2);
-  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
-  uint4 kr[CPT], vr[CPT];
-  auto gload = [&](const rsrc_t& src, int tile, uint4 (&r)[CPT]) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, tile * (BN * HD * 2) + (tid + ch * NT) * 16);
-  };
-  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
-      if (CPT * NT == BN * 8 || idx < BN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
-    }
-  };
-
-  f32x4 Sa[4][NQB], Sb[4][NQB];
-  gload(krs, 0, kr);
-  swrite(Kb[0], KP, kr);
-  __syncthreads();
-  pipe_qk<NQB>(Kb[0], Qf, col, grp, Sa);
-  if (T > 1) {
-    gload(krs, 1, kr);
-    swrite(Kb[1], KP, kr);
-  }
-  __syncthreads();
-
-  auto step = [&](auto has_next, auto has_prev, int t, f32x4 (&Scur)[4][NQB], f32x4 (&Snext)[4][NQB]) {
-    constexpr bool NEXT = decltype(has_next)::value;
-    constexpr bool PREV = decltype(has_prev)::value;
-    if (NEXT) gload(krs, t + 2, kr);
-    gload(vrs, t, vr);
-    // LDS operand reads for this step's MFMAs
-    bf16x8 kf[4][2], vf[2][4];
-    if (NEXT) {
-      const unsigned short* Kt = Kb[(t + 1) & 1];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          kf[kb4][tt] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb4 + col) * KP + 32 * tt + 8 * grp]);
-    }
-    if (PREV) {
-      const unsigned short* Vt = Vb[(t - 1) & 1];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int vcol = 16 * db + 4 * (col & 3);
-          vf[ks][db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // row maxima (the loads land meanwhile); ragged last tile masked first
-    if (!NEXT) {
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = t * BN + 16 * kb4 + 4 * grp + e < Sk;
-#pragma unroll
-          for (int i = 0; i < NQB; ++i) Scur[kb4][i][e] = ok ? Scur[kb4][i][e] : -INFINITY;
-        }
-    }
-    float alpha[NQB], mc[NQB];
-    bool any = false;
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      float mx = Scur[0][i][0];
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Scur[kb4][i][e]);
-      mx = group4_max(mx);
-      const bool raise = (mx - R.m[i]) * c > LAZY_LOG2;
-      const float mnew = raise ? mx : R.m[i];
-      alpha[i] = fast_exp2((R.m[i] - mnew) * c);
-      R.m[i] = mnew;
-      mc[i] = mnew * c;
-      any = any || raise;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // weights element by element, each beside one MFMA
-    auto weight = [&](int idx) {
-      const int i = idx % NQB, kb4 = (idx / NQB) / 4, e = (idx / NQB) % 4;
-      float x = fast_exp2(__builtin_fmaf(Scur[kb4][i][e], c, -mc[i]));
-      asm volatile("" : "+v"(x));  // computed here, beside its MFMA, not sunk past the barrier
-      Scur[kb4][i][e] = x;
-    };
-    int wi = 0;
-    if (NEXT) {
-#pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-          Snext[kb4][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb4][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          if (wi < NS) weight(wi++);
-          __builtin_amdgcn_sched_barrier(0);
-          Snext[kb4][i] = mfma_bf16(kf[kb4][1], Qf[i][1], Snext[kb4][i]);
-          if (wi < NS) weight(wi++);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    if (PREV) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < NQB; ++i) {
-            R.O[db][i] = mfma_bf16(vf[ks][db], R.P[ks][i], R.O[db][i]);
-            if (wi < NS) weight(wi++);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-          R.L[i] = mfma_bf16(ones, R.P[ks][i], R.L[i]);
-          if (wi < NS) weight(wi++);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-#pragma unroll
-    for (; wi < NS;) weight(wi++);  // tiles without enough matrix work
-    // bf16 weights for the next step's P.V
-    bf16x8 Pn[2][NQB];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) Pn[ks][i] = pack_bf16(Scur[2 * ks][i], Scur[2 * ks + 1][i]);
-    __builtin_amdgcn_sched_barrier(0);
-    pipe_rescale<NQB>(any, alpha, R);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) R.P[ks][i] = Pn[ks][i];
-    if (NEXT && t + 2 < T) swrite(Kb[t & 1], KP, kr);
-    swrite(Vb[t & 1], VP, vr);
-    __syncthreads();
-  };
-  using yes = std::integral_constant<bool, true>;
-  using no = std::integral_constant<bool, false>;
-
-  if (T == 1) {
-    step(no{}, no{}, 0, Sa, Sb);
-  } else {
-    step(yes{}, no{}, 0, Sa, Sb);
-    int t = 1;
-    for (; t + 2 <= T - 1; t += 2) {
-      step(yes{}, yes{}, t, Sb, Sa);
-      step(yes{}, yes{}, t + 1, Sa, Sb);
-    }
-    if (t < T - 1) {
-      step(yes{}, yes{}, t, Sb, Sa);
-      step(no{}, yes{}, t + 1, Sa, Sb);
-    } else {
-      step(no{}, yes{}, t, Sb, Sa);
-    }
-  }
-  pipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
-
+  const unsigned short* kb = k + bh * (size_t)Sk * HD;
+  const unsigned short* vb = v + bh * (size_t)Sk * HD;
   unsigned short* ob = o + bh * (size_t)Sq * HD;
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const float inv = 1.0f / R.L[i][0];
-    const int row = q0 + 16 * i + col;
-    if (row < Sq) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv));
-    }
-  }
+  if (w < 4)
+    duo_wave<NA>(sm, qb, Sq, base + w * 16 * NA, kb, vb, Sk, c, ob, tid);
+  else
+    duo_wave<NB>(sm, qb, Sq, base + 64 * NA + (w - 4) * 16 * NB, kb, vb, Sk, c, ob, tid);
 }
 
 // ---------------------------------------------------------------- bf16 cross (keys resident in LDS)
@@ -1122,12 +770,52 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
   return hipGetLastError();
 }
 
+namespace {
+// compute units of the current device (cached per device; 256 on MI355X)
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+template <int NA, int NB>
+hipError_t duo_launch(const unsigned short* q, const unsigned short* k, const unsigned short* v, unsigned short* o,
+                      int B, int H, int Sq, int Sk, float c, hipStream_t s) {
+  const int nqb = (int)cdiv(Sq, 64 * (NA + NB));
+  hipLaunchKernelGGL((attn_bf16_duo<NA, NB>), dim3(nqb * B * H), dim3(512), 0, s, q, k, v, o, Sq, Sk, c, B * H);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                             unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
-  // 16 queries per wave, 4 waves per block, 4 waves per SIMD: the fastest shape measured
-  // on the SDXL level-1 workload (B=2, H=10, S=4096)
-  constexpr int NQB = 1, NW = 4;
   const float c = scale * LOG2E;
+  const long long bh = (long long)B * H;
+  const int cus = cu_count();
+  if (bh * cdiv(Sq, 256) >= cus) {
+    // one 8-wave block per CU: pick the query blocks per SIMD (NA + NB) that minimise
+    // rounds x per-SIMD work, e.g. 3+3 (one round of 220 blocks) for B=2, H=10, S=4096
+    const int na[3] = {3, 3, 2}, nb[3] = {3, 2, 2};
+    int best = 0;
+    long long best_cost = -1;
+    for (int i = 0; i < 3; ++i) {
+      const long long cost = cdiv(bh * cdiv(Sq, 64 * (na[i] + nb[i])), cus) * (na[i] + nb[i]);
+      if (best_cost < 0 || cost < best_cost) { best = i; best_cost = cost; }
+    }
+    if (best == 0) return duo_launch<3, 3>(q, k, v, o, B, H, Sq, Sk, c, s);
+    if (best == 1) return duo_launch<3, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
+    return duo_launch<2, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
+  }
+  // small grids: 16 queries per wave, 4 waves per block, 4 waves per SIMD
+  constexpr int NQB = 1, NW = 4;
   const int nqb = (Sq + 16 * NQB * NW - 1) / (16 * NQB * NW);
   dim3 grid(nqb * B * H);  // one dimension: the kernel maps block -> (b, h, query block)
   hipLaunchKernelGGL((attn_bf16_pipe<NQB, NW, 0, 4>), grid, dim3(64 * NW), 0, s, q, k, v, o, Sq, Sk, c, B * H);
