@@ -76,6 +76,17 @@ def test_dense_bf16_shapes(B, H, Sq, Sk):
     assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"bf16 {B}x{H}x{Sq}x{Sk}")
 
 
+@pytest.mark.parametrize("Sq,Sk", [(370, 333), (300, 97), (250, 301), (16, 33)])
+def test_dense_bf16_eight_wave_blocks(Sq, Sk):
+    """256 (b, h) slices fill a 256-CU chip with 8-wave blocks; the query counts then select the
+    3+3 (370), 3+2 (300) and 2+2 (250, 16) block layouts, each with a ragged last query block and a
+    ragged last key tile (16 queries: most waves of the block own no valid query)."""
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = synth.make_dense(wl, seed_base=300 + Sq + Sk, B=1, H=256, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"bf16 1x256x{Sq}x{Sk}")
+
+
 def test_dense_bf16_peaked():
     """q scaled by 8: a peaked softmax, where a dropped or duplicated key tile is visible."""
     B, H, Sq, Sk = 1, 2, 256, 700
