@@ -389,16 +389,34 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 // then the block synchronises once.  Threads 0-255 stage K, 256-511 stage V, one
 // 16-byte chunk each per tile, loaded one step before it is stored.
 //
-// Lazy maximum with a vote: a lane compares the maximum of its 8 scores of a tile
-// with the threshold m + LAZY_LOG2 / c; only when some lane of the wave exceeds it
-// are the four-lane maxima taken and the reference maximum raised (the accumulator
-// rescaled after this step's P.V).  Other tiles cost one compare per block.
-constexpr int DBN = 32;  // keys per tile
+// Vector work is what bounds this loop on CDNA4 (an MFMA hides little of it), so the
+// weights take one v_exp each and nothing else but the bf16 pack:
+//   * Q is held pre-multiplied by c = scale * log2(e) (one bf16 rounding of c*q, at most
+//     2^-9 relative), and each tile's first QK product starts from -R instead of zero,
+//     so the scores arrive as c*s - R and the weight is 2^(score) directly;
+//   * R sits LAZY_LOG2 - 1 above the running maximum, so every weight stays below 2
+//     unless a score passes the maximum by LAZY_LOG2.  Weights >= 2 are the bf16 values
+//     with bit 14 set: one OR over the packed weights and a wave-wide vote replace the
+//     per-tile maximum.  Only on a vote (and on the first tile) are the four-lane maxima
+//     taken, R raised, this tile's weights recomputed, the next tile's scores (already
+//     formed against the old R) shifted, and O, l rescaled.
+// The common 2^-(LAZY_LOG2 - 1) factor of the weights cancels in O / l.
+constexpr int DBN = 32;       // keys per tile
+constexpr int DUO_VSLOT = 5;  // MFMA slot at which a step reads its V fragments
+constexpr int DUO_VLEAD = 2;  // vector work runs this many slots ahead of the MFMAs
 
 struct DuoLds {
   unsigned short K[2][DBN * KP];
   unsigned short V[2][DBN * VP];
 };
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(unsigned, v);
+}
 
 template <int NQB>
 __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __restrict__ qb, int Sq, int q0,
@@ -422,16 +440,22 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     for (int t = 0; t < 2; ++t) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
-      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
+      float f[8];
+      unpack_bf16x8(u, f);
+      Qf[i][t] = pack_bf16(f32x4{f[0] * c, f[1] * c, f[2] * c, f[3] * c}, f32x4{f[4] * c, f[5] * c, f[6] * c, f[7] * c});
     }
   }
   f32x4 O[4][NQB], L[NQB];
-  float mc[NQB], thr[NQB];  // reference maximum times c; raise threshold in score units
+  // R: exp2-domain reference, LAZY_LOG2 - 1 above the running maximum.  The first QK product of a tile
+  // starts from -R, so scores arrive as c*s - R and the weights 2^(c*s - R) stay below 2 until some score
+  // passes the maximum by LAZY_LOG2: then (and on the first tile) R is raised.
+  float R[NQB];
+  f32x4 Bq[NQB];
   bf16x8 P[NQB];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
-    mc[i] = -INFINITY;
-    thr[i] = -INFINITY;
+    R[i] = -INFINITY;
+    Bq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 4; ++db) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -439,7 +463,6 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  const float lazy_s = LAZY_LOG2 / c, inv_c = 1.0f / c;
 
   const int T = (Sk + DBN - 1) / DBN;
   uint4 st[2];
@@ -475,7 +498,10 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
         for (int h = 0; h < 2; ++h)
           kf[kb][h] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb + col) * KP + 32 * h + 8 * grp]);
     }
-    if (PREV) {
+    // V fragments are read at MFMA slot DUO_VSLOT, after the K fragments have been consumed by the first
+    // QK products; steps without QK work start their P.V products at slot 0 and read them up front
+    constexpr int VS = NEXT ? DUO_VSLOT : -1;
+    auto load_v = [&]() {
       // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
       // (keys 4*grp + e of the first 16-key half, then of the second)
       const unsigned short* Vt = sm.V[PAR ^ 1];
@@ -485,7 +511,8 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
         const int vcol = 16 * db + 4 * (col & 3);
         vf[db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
       }
-    }
+    };
+    if (PREV && VS < 0) load_v();
     if (!NEXT) {  // last tile: keys past Sk take no weight
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -496,25 +523,6 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
           for (int i = 0; i < NQB; ++i) Sc[kb][i][e] = ok ? Sc[kb][i][e] : -INFINITY;
         }
     }
-    float lmx[NQB];
-    bool exceed = false;
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      lmx[i] = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
-                     fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
-      exceed = exceed || lmx[i] > thr[i];
-    }
-    float alpha[NQB];
-    const bool raised = __builtin_amdgcn_ballot_w64(exceed) != 0;
-    if (raised) {  // true on the first tile (threshold -inf)
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) {
-        const float mcn = fmaxf(mc[i], group4_max(lmx[i]) * c);
-        alpha[i] = fast_exp2(mc[i] - mcn);  // 0 on the first tile
-        mc[i] = mcn;
-        thr[i] = __builtin_fmaf(mcn, inv_c, lazy_s);
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NQK = NEXT ? 4 * NQB : 0;
     constexpr int NM = NQK + (PREV ? 5 * NQB : 0);
@@ -523,7 +531,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       if constexpr (j < NQK) {
         constexpr int i = j / 4, kb = (j / 2) % 2, h = j % 2;
         if constexpr (h == 0)
-          Sn[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          Sn[kb][i] = mfma_bf16(kf[kb][0], Qf[i][0], Bq[i]);
         else
           Sn[kb][i] = mfma_bf16(kf[kb][1], Qf[i][1], Sn[kb][i]);
       } else if constexpr (j < NM) {
@@ -534,40 +542,68 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
           L[i] = mfma_bf16(ones, P[i], L[i]);
       }
     };
-    bf16x8 Pn[NQB];
+    unsigned Pw[NQB][4];
+    float xe[NQB];
+    unsigned orb = 0;
     auto valu_at = [&](auto ss) {
       constexpr int s = decltype(ss)::value;
       constexpr int i = s / 9, e = s % 9;
       if constexpr (i < NQB) {
         if constexpr (e < 8) {
-          float x = fast_exp2(__builtin_fmaf(Sc[e >> 2][i][e & 3], c, -mc[i]));
+          float x = fast_exp2(Sc[e >> 2][i][e & 3]);
           asm volatile("" : "+v"(x));  // computed in its slot, not sunk past the next barrier
-          Sc[e >> 2][i][e & 3] = x;
+          if constexpr (e & 1) {
+            Pw[i][e >> 1] = cvt2_bf16(xe[i], x);
+            asm volatile("" : "+v"(Pw[i][e >> 1]));
+          } else {
+            xe[i] = x;
+          }
         } else {
-          Pn[i] = pack_bf16(Sc[0][i], Sc[1][i]);
-          asm volatile("" : "+v"(Pn[i]));
+          orb |= Pw[i][0] | Pw[i][1] | Pw[i][2] | Pw[i][3];
         }
       }
     };
-    // slot s: MFMA s, then vector work s (8 weights and one pack per query block)
-    constexpr int NSLOT = (NM > 9 * NQB) ? NM : 9 * NQB;
+    // slot s: MFMA s - DUO_VLEAD, then vector work s (8 weights, packed in pairs, and one OR per query
+    // block): the first slots hold only weights, which need no LDS data, while the K fragments arrive
+    constexpr int NSLOT = (NM + DUO_VLEAD > 9 * NQB) ? NM + DUO_VLEAD : 9 * NQB;
     [&]<int... S>(std::integer_sequence<int, S...>) {
       ([&] {
-        mfma_at(std::integral_constant<int, S>{});
+        constexpr int SM = S - DUO_VLEAD;
+        if constexpr (SM >= 0) mfma_at(std::integral_constant<int, SM>{});
+        if constexpr (PREV && VS >= 0 && SM == VS) load_v();
         valu_at(std::integral_constant<int, S>{});
         __builtin_amdgcn_sched_barrier(0);
       }(), ...);
     }(std::make_integer_sequence<int, NSLOT>{});
+    // some weight of this tile reached 2 (bit 14 of a bf16 half), or first tile
+    const bool raised = !PREV || __builtin_amdgcn_ballot_w64((orb & 0x40004000u) != 0) != 0;
     if (raised) {
 #pragma unroll
       for (int i = 0; i < NQB; ++i) {
+        const float lmx = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
+                                fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
+        const float base = PREV ? R[i] : 0.f;  // the reference these scores were formed against
+        const float Rn = fmaxf(R[i], base + group4_max(lmx) + (LAZY_LOG2 - 1.f));
+        const float alpha = fast_exp2(R[i] - Rn);  // 0 on the first tile
+        const float d = Rn - base;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) O[db][i] *= alpha[i];
-        L[i] *= alpha[i];
+        for (int h = 0; h < 4; ++h)
+          Pw[i][h] = cvt2_bf16(fast_exp2(Sc[h >> 1][i][2 * (h & 1)] - d), fast_exp2(Sc[h >> 1][i][2 * (h & 1) + 1] - d));
+        if constexpr (NEXT) {  // the next tile's scores were formed against `base` too
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sn[kb][i][e] -= d;
+        }
+        R[i] = Rn;
+        Bq[i] = f32x4{-Rn, -Rn, -Rn, -Rn};
+#pragma unroll
+        for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
+        L[i] *= alpha;
       }
     }
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) P[i] = Pn[i];
+    for (int i = 0; i < NQB; ++i) P[i] = __builtin_bit_cast(bf16x8, make_uint4(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]));
     if (t + lead < T) st16(PAR ? sdst1 : sdst0, st[PAR]);
     __syncthreads();
   };
