@@ -33,6 +33,7 @@
 //   * the running maximum is raised lazily (LAZY_LOG2 in ka_common.hpp).
 // This file is compiled without NaN semantics (-fno-honor-nans): the maxima are
 // taken on finite scores or -inf, and IEEE NaN quieting would double their cost.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -404,6 +405,7 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 constexpr int DBN = 32;       // keys per tile
 constexpr int DUO_VSLOT = 5;  // MFMA slot at which a step reads its V fragments
 constexpr int DUO_VLEAD = 2;  // vector work runs this many slots ahead of the MFMAs
+constexpr int DUO_STG = 4;    // 4-wave form: vector slot at which the staged K / V are stored
 
 struct DuoLds {
   unsigned short K[2][DBN * KP];
@@ -418,19 +420,27 @@ __device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-template <int NQB>
+// QUAD = false: 512-thread block, threads 0-255 stage K and 256-511 stage V, each tile
+// loaded one step before it is stored (two staging registers).  QUAD = true: 256-thread
+// block, every thread stages one K and one V chunk per tile, loaded right after the
+// previous store so that one staging register per stream suffices.
+template <int NQB, bool QUAD>
 __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __restrict__ qb, int Sq, int q0,
                                          const unsigned short* kbase, const unsigned short* vbase, int Sk, float c,
                                          unsigned short* __restrict__ ob, int tid) {
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const bool isK = tid < 256;
+  const bool isK = QUAD || tid < 256;
   const int chunk = tid & 255, srow = chunk >> 3, scol = (chunk & 7) * 8;
   // rows past Sk read as zero through the buffer resource
   const rsrc_t srs = make_rsrc(isK ? kbase : vbase, Sk * HD * 2);
+  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
   const int lead = isK ? 2 : 0;  // step t stores tile t + lead and loads tile t + lead + 1
   unsigned short* sdst0 = isK ? &sm.K[0][srow * KP + scol] : &sm.V[0][srow * VP + scol];
   unsigned short* sdst1 = isK ? &sm.K[1][srow * KP + scol] : &sm.V[1][srow * VP + scol];
+  unsigned short* vdst0 = &sm.V[0][srow * VP + scol];
+  unsigned short* vdst1 = &sm.V[1][srow * VP + scol];
   auto ldt = [&](int tile) { return buf_ld16(srs, tile * (DBN * HD * 2) + chunk * 16); };
+  auto ldv = [&](int tile) { return buf_ld16(vrs, tile * (DBN * HD * 2) + chunk * 16); };
 
   bf16x8 Qf[NQB][2];
 #pragma unroll
@@ -465,7 +475,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   const int T = (Sk + DBN - 1) / DBN;
-  uint4 st[2];
+  uint4 st[2], stv;
   f32x4 Sa[2][NQB], Sb[2][NQB];
   // prologue: K(0) -> K[0], S(0) = K(0) Q^T; K(1) -> K[1]; stage K(2) / V(0)
   if (isK) st16(sdst0, ldt(0));
@@ -482,13 +492,14 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   }
   if (isK && T > 1) st16(sdst1, ldt(1));
   st[0] = ldt(lead);
+  if constexpr (QUAD) stv = ldv(0);
   __syncthreads();
 
   auto step = [&](auto has_next, auto has_prev, auto parity, int t, f32x4 (&Sc)[2][NQB], f32x4 (&Sn)[2][NQB]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
     constexpr int PAR = decltype(parity)::value;  // t & 1
-    st[PAR ^ 1] = ldt(t + lead + 1);  // past the last tile: zeros, never stored
+    if constexpr (!QUAD) st[PAR ^ 1] = ldt(t + lead + 1);  // past the last tile: zeros, never stored
     bf16x8 kf[2][2], vf[4];
     if (NEXT) {
       const unsigned short* Kt = sm.K[PAR ^ 1];
@@ -571,6 +582,13 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
         constexpr int SM = S - DUO_VLEAD;
         if constexpr (SM >= 0) mfma_at(std::integral_constant<int, SM>{});
         if constexpr (PREV && VS >= 0 && SM == VS) load_v();
+        if constexpr (QUAD && S == (DUO_STG < NSLOT ? DUO_STG : NSLOT - 1)) {
+          // the ring slots written here were last read in step t - 1
+          if (t + 2 < T) st16(PAR ? sdst1 : sdst0, st[0]);
+          st16(PAR ? vdst1 : vdst0, stv);
+          st[0] = ldt(t + 3);  // past the last tile: zeros, never stored
+          stv = ldv(t + 1);
+        }
         valu_at(std::integral_constant<int, S>{});
         __builtin_amdgcn_sched_barrier(0);
       }(), ...);
@@ -604,7 +622,9 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     }
 #pragma unroll
     for (int i = 0; i < NQB; ++i) P[i] = __builtin_bit_cast(bf16x8, make_uint4(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]));
-    if (t + lead < T) st16(PAR ? sdst1 : sdst0, st[PAR]);
+    if constexpr (!QUAD) {
+      if (t + lead < T) st16(PAR ? sdst1 : sdst0, st[PAR]);
+    }
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
@@ -673,9 +693,60 @@ void attn_bf16_duo(const unsigned short* __restrict__ q, const unsigned short* _
   const unsigned short* vb = v + bh * (size_t)Sk * HD;
   unsigned short* ob = o + bh * (size_t)Sq * HD;
   if (w < 4)
-    duo_wave<NA>(sm, qb, Sq, base + w * 16 * NA, kb, vb, Sk, c, ob, tid);
+    duo_wave<NA, false>(sm, qb, Sq, base + w * 16 * NA, kb, vb, Sk, c, ob, tid);
   else
-    duo_wave<NB>(sm, qb, Sq, base + 64 * NA + (w - 4) * 16 * NB, kb, vb, Sk, c, ob, tid);
+    duo_wave<NB, false>(sm, qb, Sq, base + 64 * NA + (w - 4) * 16 * NB, kb, vb, Sk, c, ob, tid);
+}
+
+// 4-wave blocks, two per CU, for grids that fit one round: the launcher splits every head
+// into items of s0 or s1 query units (a unit = one 16-query block per wave = 64 queries),
+// round 0 (blocks [0, C)) takes the s0-items and round 1 the s1-items, so that block i and
+// block i + C, which the dispatcher places on one CU, carry s0 + s1 units per SIMD.
+// Heads [0, nX) split into aX s0-items and bX s1-items, the others into aY and bY.
+struct QuadPlan {
+  int c8;             // CUs / 8
+  int s0, s1;         // units per item of round 0 / 1
+  int nX, aX, bX, aY, bY;
+  int cnt0, cnt1;     // items in round 0 / 1
+};
+
+__device__ __forceinline__ int quad_items(const QuadPlan& p, int r, int h) {
+  return r == 0 ? (h < p.nX ? p.aX : p.aY) : (h < p.nX ? p.bX : p.bY);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_quad(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
+                    const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                    QuadPlan p) {
+  __shared__ __align__(16) DuoLds sm;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int C = 8 * p.c8, r = blockIdx.x >= C, pi = blockIdx.x - r * C;
+  // XCD-aware: block pi runs on XCD pi % 8, which takes items [c8 * (pi % 8), c8 * (pi % 8 + 1))
+  const int l = (pi & 7) * p.c8 + (pi >> 3);
+  if (l >= (r ? p.cnt1 : p.cnt0)) return;
+  const int ax = quad_items(p, r, 0), ay = quad_items(p, r, p.nX);
+  int h, j;
+  if (l < p.nX * ax) {
+    h = l / ax;
+    j = l - h * ax;
+  } else {
+    const int l2 = l - p.nX * ax;
+    h = p.nX + l2 / ay;
+    j = l2 - (h - p.nX) * ay;
+  }
+  const int s = r ? p.s1 : p.s0;
+  const int q0 = 64 * ((r ? quad_items(p, 0, h) * p.s0 : 0) + j * s);
+  const size_t bh = h;
+  const unsigned short* qb = q + bh * (size_t)Sq * HD;
+  const unsigned short* kb = k + bh * (size_t)Sk * HD;
+  const unsigned short* vb = v + bh * (size_t)Sk * HD;
+  unsigned short* ob = o + bh * (size_t)Sq * HD;
+  if (s == 3)
+    duo_wave<3, true>(sm, qb, Sq, q0 + w * 48, kb, vb, Sk, c, ob, tid);
+  else if (s == 2)
+    duo_wave<2, true>(sm, qb, Sq, q0 + w * 32, kb, vb, Sk, c, ob, tid);
+  else
+    duo_wave<1, true>(sm, qb, Sq, q0 + w * 16, kb, vb, Sk, c, ob, tid);
 }
 
 // ---------------------------------------------------------------- bf16 cross (keys resident in LDS)
@@ -822,6 +893,17 @@ int cu_count() {
 
 long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+// per-SIMD query blocks x rounds of the best attn_bf16_duo layout, times the CU count
+long long duo_cost(long long bh, int Sq, int cus) {
+  const int na[3] = {3, 3, 2}, nb[3] = {3, 2, 2};
+  long long best = -1;
+  for (int i = 0; i < 3; ++i) {
+    const long long cost = cdiv(bh * cdiv(Sq, 64 * (na[i] + nb[i])), cus) * (na[i] + nb[i]) * cus;
+    if (best < 0 || cost < best) best = cost;
+  }
+  return best;
+}
+
 template <int NA, int NB>
 hipError_t duo_launch(const unsigned short* q, const unsigned short* k, const unsigned short* v, unsigned short* o,
                       int B, int H, int Sq, int Sk, float c, hipStream_t s) {
@@ -831,11 +913,62 @@ hipError_t duo_launch(const unsigned short* q, const unsigned short* k, const un
 }
 }  // namespace
 
+// One-round plan for attn_bf16_quad: with U units per head and W = U * BH in all, each CU
+// gets L = ceil(W / C) units per SIMD as an s0-item plus an s1-item.  Heads split into
+// (aX, bX) or (aY, bY) items with s0 a + s1 b >= U; the counts must fit C per round.
+// Least padding first, then the closest pair of splits: with every head split alike, the
+// round-0 and round-1 items that an XCD takes come from the same heads (shared K / V in L2).
+static bool quad_plan_search(long long bh, int Sq, int cus, QuadPlan& p) {
+  if (cus % 8 != 0 || bh > 4 * (long long)cus) return false;
+  const int U = (int)cdiv(Sq, 64);
+  const long long L = cdiv(U * bh, cus);
+  if (L < 4 || L > 6) return false;
+  const int s0 = L == 4 ? 2 : 3, s1 = (int)L - s0;
+  long long best = -1;
+  const int amax = (int)cdiv(U, s0);
+  for (int aX = 0; aX <= amax; ++aX)
+    for (int aY = aX; aY <= amax; ++aY) {
+      const int bX = (int)std::max(0LL, cdiv(U - s0 * aX, s1)), bY = (int)std::max(0LL, cdiv(U - s0 * aY, s1));
+      for (long long nX = 0; nX <= bh; ++nX) {
+        const long long A = nX * aX + (bh - nX) * aY, Bn = nX * bX + (bh - nX) * bY;
+        if (A > cus || Bn > cus) continue;
+        const long long waste = nX * (s0 * aX + s1 * bX) + (bh - nX) * (s0 * aY + s1 * bY) - U * bh;
+        const long long score = waste * (amax + 1) + (aY - aX);
+        if (best < 0 || score < best) {
+          best = score;
+          p = QuadPlan{cus / 8, s0, s1, (int)nX, aX, bX, aY, bY, (int)A, (int)Bn};
+        }
+      }
+    }
+  return best >= 0;
+}
+
+// the search is small (L <= 6 bounds U * BH) but runs per launch: remember the last shape
+static bool quad_plan(long long bh, int Sq, int cus, QuadPlan& p) {
+  thread_local long long key_bh = -1;
+  thread_local int key_sq = -1, key_cus = -1;
+  thread_local bool ok = false;
+  thread_local QuadPlan plan{};
+  if (bh != key_bh || Sq != key_sq || cus != key_cus) {
+    ok = quad_plan_search(bh, Sq, cus, plan);
+    key_bh = bh;
+    key_sq = Sq;
+    key_cus = cus;
+  }
+  p = plan;
+  return ok;
+}
+
 hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                             unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
   const float c = scale * LOG2E;
   const long long bh = (long long)B * H;
   const int cus = cu_count();
+  QuadPlan plan;
+  if (quad_plan(bh, Sq, cus, plan) && (long long)(plan.s0 + plan.s1) * cus < duo_cost(bh, Sq, cus)) {
+    hipLaunchKernelGGL(attn_bf16_quad, dim3(2 * cus), dim3(256), 0, s, q, k, v, o, Sq, Sk, c, plan);
+    return hipGetLastError();
+  }
   if (bh * cdiv(Sq, 256) >= cus) {
     // one 8-wave block per CU: pick the query blocks per SIMD (NA + NB) that minimise
     // rounds x per-SIMD work, e.g. 3+3 (one round of 220 blocks) for B=2, H=10, S=4096

@@ -87,6 +87,18 @@ def test_dense_bf16_eight_wave_blocks(Sq, Sk):
     assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"bf16 1x256x{Sq}x{Sk}")
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk", [(1, 13, 4900, 333), (2, 10, 4000, 1000), (2, 12, 3900, 77), (2, 10, 4000, 20)])
+def test_dense_bf16_four_wave_blocks(B, H, Sq, Sk):
+    """Grids whose 8-wave layouts leave CUs idle go to 4-wave blocks, two per CU, with the heads split
+    into 2- and 3-unit items (a unit: 64 queries).  On a 256-CU chip these shapes select the 2+2
+    (4900), 3+2 (4000) and 3+3 (3900) unit plans, with ragged last items and key tiles, idle blocks
+    (fewer items than CUs in a round) and a single key tile (Sk = 20)."""
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    q, k, v = synth.make_dense(wl, seed_base=500 + H + Sq + Sk, B=B, H=H, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"bf16 {B}x{H}x{Sq}x{Sk}")
+
+
 def test_dense_bf16_peaked():
     """q scaled by 8: a peaked softmax, where a dropped or duplicated key tile is visible."""
     B, H, Sq, Sk = 1, 2, 256, 700
@@ -102,7 +114,7 @@ def test_dense_bf16_workload_sampled():
     wl = W["sdxl_l1_self_b2h10s4096"]
     q, k, v = synth.make_dense(wl)
     got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale).reshape(-1, D)
-    rows = _rows_sample(wl.B, wl.H, wl.Sq, 400, 11, edge=2, period=128)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 400, 11, edge=2, period=64)  # every item boundary
     r = assert_close(got[rows], oracle.attn(q, k, v, wl.scale, rows=rows), BF16_TOL, wl.key)
     assert r["rel_rms"] < 1e-2
 
