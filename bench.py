@@ -74,8 +74,9 @@ def time_launches(fn, nsets, steps, warmup, torch):
 
 def time_graph(fn, nsets, steps, warmup, torch):
     """Like time_launches, with the `steps` launches captured once into a HIP graph and replayed,
-    so that host-side call overhead does not hide kernels shorter than it."""
-    prewarm(fn, nsets, PREWARM_S, torch)
+    so that host-side call overhead does not hide kernels shorter than it.  The untimed warm-up
+    replays the same graph for PREWARM_S of wall time: launches from Python cannot keep a kernel of
+    a few tens of microseconds back to back, and at a partial duty cycle the clock stays low."""
     for i in range(warmup):
         fn(i % nsets)
     torch.cuda.synchronize()
@@ -86,8 +87,12 @@ def time_graph(fn, nsets, steps, warmup, torch):
             for i in range(steps):
                 fn(i % nsets)
     torch.cuda.synchronize()
-    g.replay()  # warm replay
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= PREWARM_S:
+            break
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)

@@ -73,15 +73,20 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
                                             int tb, const SharedParams& sp) {
   const float ka = sp.k2a[ta], kb = sp.k2a[tb];
   const float pf = (float)p;
-  const bool split = sp.split;
+  // one uniform branch for all eight angles, so that the straight-line DyT and rotation
+  // below form one block the scheduler can interleave
+  float csv[8], snv[8];
+  if (sp.split) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_cs_split(pf, sp.rev_hi[i0 + e], sp.rev_lo[i0 + e], csv[e], snv[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_cs_f64(p, sp.rev[i0 + e], csv[e], snv[e]);
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int i = i0 + e;
-    float cs, sn;
-    if (split)
-      rope_cs_split(pf, sp.rev_hi[i], sp.rev_lo[i], cs, sn);
-    else
-      rope_cs_f64(p, sp.rev[i], cs, sn);
+    const float cs = csv[e], sn = snv[e];
     const float a0 = dyt(alo[e], ka, sp.gpb[ta][i], sp.m2g[ta][i]);
     const float a1 = dyt(ahi[e], ka, sp.gpb[ta][i + 32], sp.m2g[ta][i + 32]);
     // explicit fused forms: every tensor rounds identically, whatever the compiler would contract
@@ -133,28 +138,30 @@ struct RowStage {
   uint4 k1lo, k1hi, k2lo, k2hi, v0, v1;
 };
 
-__device__ __forceinline__ void stage_load(RowStage& st, const DiffArgs& a, size_t base, int j, bool ok, int cc) {
-  st.k1lo = st.k1hi = st.k2lo = st.k2hi = st.v0 = st.v1 = make_uint4(0, 0, 0, 0);
-  if (ok) {
-    const size_t off = base + (size_t)j * HD;
-    st.k1lo = ld16(a.k1 + off + 8 * cc);
-    st.k1hi = ld16(a.k1 + off + 32 + 8 * cc);
-    st.k2lo = ld16(a.k2 + off + 8 * cc);
-    st.k2hi = ld16(a.k2 + off + 32 + 8 * cc);
-    st.v0 = ld16(a.v + off + 16 * cc);
-    st.v1 = ld16(a.v + off + 16 * cc + 8);
-  }
+// Rows j outside [0, S) read as zero through the buffer resources (a negative row
+// offset wraps past the end), so no lane branches.
+struct BandSrc {
+  rsrc_t k1, k2, v;
+};
+__device__ __forceinline__ void stage_load(RowStage& st, const BandSrc& src, int j, int cc) {
+  const int off = j * (HD * 2);
+  st.k1lo = buf_ld16(src.k1, off + 16 * cc);
+  st.k1hi = buf_ld16(src.k1, off + 64 + 16 * cc);
+  st.k2lo = buf_ld16(src.k2, off + 16 * cc);
+  st.k2hi = buf_ld16(src.k2, off + 64 + 16 * cc);
+  st.v0 = buf_ld16(src.v, off + 32 * cc);
+  st.v1 = buf_ld16(src.v, off + 32 * cc + 16);
 }
 
 __device__ __forceinline__ void stage_commit(const RowStage& st, unsigned short* K1s, unsigned short* K2s,
-                                             unsigned short* Vs, int slot, int j, bool ok, int cc,
-                                             const SharedParams& sp) {
+                                             unsigned short* Vs, int slot, int j, int cc, const SharedParams& sp) {
   float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
   unpack_bf16x8(st.k1lo, k1lo);
   unpack_bf16x8(st.k1hi, k1hi);
   unpack_bf16x8(st.k2lo, k2lo);
   unpack_bf16x8(st.k2hi, k2hi);
-  if (ok) prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);  // rows outside stay zero
+  // rows no query of the strip sees are prepared too (finite, and masked in every tile)
+  prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);
   st16(&K1s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1lo)));
   st16(&K1s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1hi)));
   st16(&K2s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2lo)));
@@ -168,8 +175,9 @@ __device__ __forceinline__ void stage_commit(const RowStage& st, unsigned short*
 // all-ones MFMA over the same bf16 weights.
 template <int NKB, int NR>
 __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsigned short* Vs, int s0,
-                                            const f16x8 (&Qf)[2], const bool (&ok)[NKB][4], float c, int col,
-                                            int grp, const bf16x8& ones, f32x4 (&O)[4], float& l) {
+                                            const f16x8 (&Qf)[2], const bool (&band)[NKB][4], bool edge, int jbase,
+                                            int S, float c, int col, int grp, const bf16x8& ones, f32x4 (&O)[4],
+                                            float& l) {
   f32x4 Sc[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -180,14 +188,25 @@ __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsi
     Sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     Sc[kb] = mfma_f16(a1, Qf[1], Sc[kb]);
   }
+  // the band mask is fixed per lane; keys outside [0, S) occur only in tiles at either end
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Sc[kb][e] = band[kb][e] ? Sc[kb][e] : -INFINITY;
+  if (edge) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jbase + 16 * kb + 4 * grp + e;
+        Sc[kb][e] = (j >= 0 && j < S) ? Sc[kb][e] : -INFINITY;
+      }
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Sc[kb][e] = ok[kb][e] ? Sc[kb][e] : -INFINITY;
-      mx = fmaxf(mx, Sc[kb][e]);
-    }
+    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Sc[kb][e]);
   const float mc = group4_max(mx) * c;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -224,7 +243,7 @@ void diff_band(DiffArgs a, int nblk) {
   __shared__ __align__(16) unsigned short Vs[NR * VPD];
   __shared__ SharedParams sp;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4, cc = tid & 3;
   const int S = a.S, window = a.window;
   const size_t bh = blockIdx.y;
@@ -232,19 +251,19 @@ void diff_band(DiffArgs a, int nblk) {
   const size_t base = bh * (size_t)S * HD;
   const int strip0 = blockIdx.x * nblk * BAND_BM;
   const int pos0 = strip0 - HALO;  // position held by ring slot 0
-  // every key any query of the strip can see; other rows are kept zero (and masked)
-  const int send = min(S, strip0 + nblk * BAND_BM);
-  const int jlo = max(0, strip0 - window), jhi = min(S - 1, send - 1 + window);
+  // one (b, h) slice of each tensor; rows outside [0, S) read as zero
+  const int rbytes = S * HD * 2;
+  const BandSrc src{make_rsrc(a.k1 + base, rbytes), make_rsrc(a.k2 + base, rbytes), make_rsrc(a.v + base, rbytes)};
+  const rsrc_t q1rs = make_rsrc(a.q1 + base, rbytes), q2rs = make_rsrc(a.q2 + base, rbytes);
   load_params(sp, a);
   __syncthreads();
 
   // fill the ring for the first block: positions pos0 .. pos0 + NR - 1
   for (int r = tid >> 2; r < NR; r += 64 * BAND_NW / 4) {
     const int j = pos0 + r;
-    const bool ok = j >= jlo && j <= jhi;
     RowStage st;
-    stage_load(st, a, base, j, ok, cc);
-    stage_commit(st, K1s, K2s, Vs, r, j, ok, cc, sp);
+    stage_load(st, src, j, cc);
+    stage_commit(st, K1s, K2s, Vs, r, j, cc, sp);
   }
 
   // band mask by relative position: key j = q0 - HALO + 16kb + 4grp + e against
@@ -265,15 +284,11 @@ void diff_band(DiffArgs a, int nblk) {
   // queries of this wave for block 0
   uint4 qs[4];
   auto qload = [&](int r0) {
-    const int p = r0 + 16 * w + col;
-    qs[0] = qs[1] = qs[2] = qs[3] = make_uint4(0, 0, 0, 0);
-    if (p < S) {
-      const size_t off = base + (size_t)p * HD;
-      qs[0] = ld16(a.q1 + off + 8 * grp);
-      qs[1] = ld16(a.q1 + off + 32 + 8 * grp);
-      qs[2] = ld16(a.q2 + off + 8 * grp);
-      qs[3] = ld16(a.q2 + off + 32 + 8 * grp);
-    }
+    const int off = (r0 + 16 * w + col) * (HD * 2) + 16 * grp;  // rows past S read as zero
+    qs[0] = buf_ld16(q1rs, off);
+    qs[1] = buf_ld16(q1rs, off + 64);
+    qs[2] = buf_ld16(q2rs, off);
+    qs[3] = buf_ld16(q2rs, off + 64);
   };
   qload(strip0);
   __syncthreads();
@@ -294,28 +309,19 @@ void diff_band(DiffArgs a, int nblk) {
     const f16x8 Q2[2] = {to_f16x8(q2lo), to_f16x8(q2hi)};
     // fetch what the next block adds while this one computes
     const int jn = r0 + BAND_BM + HALO + (tid >> 2);
-    const bool okn = more && jn >= jlo && jn <= jhi;
     RowStage st;
-    stage_load(st, a, base, jn, okn, cc);
+    if (more) stage_load(st, src, jn, cc);
     if (more) qload(r0 + BAND_BM);
 
     const int jbase = q0 - HALO;
-    bool ok[NKB][4];
-    const bool edge = jbase < 0 || jbase + 16 * NKB > S;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jbase + 16 * kb + 4 * grp + e;
-        ok[kb][e] = band[kb][e] && (!edge || (j >= 0 && j < S));
-      }
+    const bool edge = jbase < 0 || jbase + 16 * NKB > S;  // uniform per wave
     const int s0 = (jbase - pos0) % NR;
     f32x4 O1[4], O2[4];
     float l1, l2;
-    band_branch<NKB, NR>(K1s, Vs, s0, Q1, ok, a.c, col, grp, ones, O1, l1);
-    band_branch<NKB, NR>(K2s, Vs, s0, Q2, ok, a.c, col, grp, ones, O2, l2);
+    band_branch<NKB, NR>(K1s, Vs, s0, Q1, band, edge, jbase, S, a.c, col, grp, ones, O1, l1);
+    band_branch<NKB, NR>(K2s, Vs, s0, Q2, band, edge, jbase, S, a.c, col, grp, ones, O2, l2);
     if (p < S) {
-      const float i1 = 1.0f / l1, i2 = lam / l2;
+      const float i1 = __builtin_amdgcn_rcpf(l1), i2 = lam * __builtin_amdgcn_rcpf(l2);
       unsigned short* orow = a.o + base + (size_t)p * HD;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -327,7 +333,7 @@ void diff_band(DiffArgs a, int nblk) {
     }
     if (more) {
       __syncthreads();  // every wave is done with the rows about to be replaced
-      stage_commit(st, K1s, K2s, Vs, (jn - pos0) % NR, jn, okn, cc, sp);
+      stage_commit(st, K1s, K2s, Vs, (jn - pos0) % NR, jn, cc, sp);
       __syncthreads();
     }
   }
