@@ -55,6 +55,15 @@ def _bind(lib):
     lib.ora_diffattn.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_double, ctypes.c_int, dp, dp, dp, ctypes.c_double, dp, ip, ctypes.c_int64]
     lib.ora_diffattn.restype = ctypes.c_int
+    u8p = ctypes.POINTER(ctypes.c_ubyte)
+    lib.ora_diffattn_ex.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_double, ctypes.c_int, ctypes.c_int, dp, dp, dp, ctypes.c_double, dp,
+                                    ctypes.c_int, ctypes.c_double, dp, u8p, ip, ctypes.c_int64]
+    lib.ora_diffattn_ex.restype = ctypes.c_int
+    lib.ora_rmsnorm_row.argtypes = [dp, ctypes.c_int, ctypes.c_double, dp, dp]
+    lib.ora_rmsnorm_row.restype = None
+    lib.ora_rope_row_partial.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_long, ctypes.c_double, dp]
+    lib.ora_rope_row_partial.restype = None
     lib.ora_dyt_row.argtypes = [dp, ctypes.c_int, ctypes.c_double, dp, dp, dp]
     lib.ora_dyt_row.restype = None
     lib.ora_rope_row.argtypes = [dp, ctypes.c_int, ctypes.c_long, ctypes.c_double, dp]
@@ -110,25 +119,51 @@ def attn(q, k, v, scale: float, rows=None, lib=None) -> np.ndarray:
 
 
 def diffattn(q1, k1, q2, k2, v, scale: float, window: int, alpha, gamma, beta, base: float, lam, rows=None,
-             lib=None) -> np.ndarray:
-    """Differential attention: O = softmax(q1^ k1^T) V - lam_h softmax(q2^ k2^T) V.
+             lib=None, norm: str = "dyt", rms_weight=None, rms_eps: float = 0.0, rotary_dims: int | None = None,
+             v_keep=None) -> np.ndarray:
+    """Differential attention: O = softmax(q1^ k1^T) V' - lam_h softmax(q2^ k2^T) V'.
 
-    q^/k^ = RoPE(DyT(.)); window >= 0 keeps keys with |i - j| <= window, window < 0 keeps all.
-    alpha [4], gamma/beta [4, D] for (q1, k1, q2, k2); lam [H].
+    q^/k^ = RoPE(Norm(.)); window >= 0 keeps keys with |i - j| <= window, window < 0 keeps all.
+    norm "dyt": alpha [4], gamma/beta [4, D] for (q1, k1, q2, k2).  norm "rms": rms_weight [4, D]
+    and rms_eps (alpha, gamma, beta may be None).  rotary_dims: the rotated width (default D).
+    v_keep: optional [B, S] flags; V' zeroes the V rows of tokens whose flag is 0 (their keys stay).
+    lam [H].  With the defaults this is the DyT form over all D dims ("ora_diffattn").
     """
     lib = lib or load()
     q1, k1, q2, k2, v = (_c64(t) for t in (q1, k1, q2, k2, v))
     B, H, S, D = q1.shape
     for t in (k1, q2, k2, v):
         assert t.shape == (B, H, S, D)
-    a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float64).reshape(4))
-    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(4, D))
-    b_ = np.ascontiguousarray(np.asarray(beta, dtype=np.float64).reshape(4, D))
     lm = np.ascontiguousarray(np.asarray(lam, dtype=np.float64).reshape(H))
     out = np.full((B, H, S, D), np.nan)
     r, rp, nr = _rows(rows)
-    rc = lib.ora_diffattn(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out), B, H, S, D, float(scale),
-                          int(window), _ptr(a), _ptr(g), _ptr(b_), float(base), _ptr(lm), rp, nr)
+    if norm == "dyt" and rotary_dims in (None, D) and v_keep is None:
+        a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float64).reshape(4))
+        g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(4, D))
+        b_ = np.ascontiguousarray(np.asarray(beta, dtype=np.float64).reshape(4, D))
+        rc = lib.ora_diffattn(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out), B, H, S, D, float(scale),
+                              int(window), _ptr(a), _ptr(g), _ptr(b_), float(base), _ptr(lm), rp, nr)
+    else:
+        null = ctypes.POINTER(ctypes.c_double)()
+        if norm == "dyt":
+            a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float64).reshape(4))
+            g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float64).reshape(4, D))
+            b_ = np.ascontiguousarray(np.asarray(beta, dtype=np.float64).reshape(4, D))
+            pa, pg, pb, pw, nid = _ptr(a), _ptr(g), _ptr(b_), null, 0
+        elif norm == "rms":
+            w = np.ascontiguousarray(np.asarray(rms_weight, dtype=np.float64).reshape(4, D))
+            pa, pg, pb, pw, nid = null, null, null, _ptr(w), 1
+        else:
+            raise ValueError(f"unknown norm {norm!r}")
+        keep = None
+        pk = ctypes.POINTER(ctypes.c_ubyte)()
+        if v_keep is not None:
+            keep = np.ascontiguousarray((np.asarray(v_keep).reshape(B, S) != 0).astype(np.uint8))
+            pk = keep.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte))
+        rot = D if rotary_dims is None else int(rotary_dims)
+        rc = lib.ora_diffattn_ex(_ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(out), B, H, S, D, float(scale),
+                                 int(window), nid, pa, pg, pb, float(rms_eps), pw, rot, float(base), _ptr(lm), pk, rp,
+                                 nr)
     if rc != 0:
         raise RuntimeError(f"ora_diffattn failed ({rc})")
     return out if r is None else out.reshape(-1, D)[r]
@@ -150,6 +185,23 @@ def rope_row(x, p: int, base: float, lib=None) -> np.ndarray:
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
     y = np.empty(x.size)
     lib.ora_rope_row(_ptr(x), x.size, int(p), float(base), _ptr(y))
+    return y
+
+
+def rmsnorm_row(x, eps: float, weight, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    w = np.ascontiguousarray(np.asarray(weight, dtype=np.float64).reshape(x.size))
+    y = np.empty(x.size)
+    lib.ora_rmsnorm_row(_ptr(x), x.size, float(eps), _ptr(w), _ptr(y))
+    return y
+
+
+def rope_row_partial(x, rot: int, p: int, base: float, lib=None) -> np.ndarray:
+    lib = lib or load()
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    y = np.empty(x.size)
+    lib.ora_rope_row_partial(_ptr(x), x.size, int(rot), int(p), float(base), _ptr(y))
     return y
 
 

@@ -27,6 +27,13 @@
  *  - The DyT formula gamma*tanh(alpha*x)+beta, the rotary width (all 64 dims,
  *    pairs (i, i+32)), base 10000, and the per-head weight lambda on branch 2 are
  *    not defined on the pages; they are the readings this library adopts.
+ *  - The Stable Audio 3 model's own forms (same page, appendix D1, D3, D4, E1):
+ *    per-head RMSNorm on q and k in place of DyT; rotary embedding on part of
+ *    the head only (rotate-half pairs d with d+16, the other dims pass through
+ *    with cos 1, sin 0: a rotary width of 32); and a padding mask that zeroes V
+ *    for padded tokens while their keys stay in the softmax.  RMSNorm's formula
+ *    (x / sqrt(mean x^2 + eps), times a learned weight per dim) and eps are not
+ *    on the pages; the standard definition is the reading taken.
  *
  * Softmax is two-pass (max, then exp and sum), the textbook stable form; the
  * online (running-max) form used by the GPU reaches the same value in exact
@@ -62,6 +69,28 @@ void ora_rope_row(const double* x, int D, long p, double base, double* y) {
     double c = cos(theta), s = sin(theta);
     y[i] = x[i] * c - x[i + half] * s;
     y[i + half] = x[i + half] * c + x[i] * s;
+  }
+}
+
+/* RMSNorm of one head row: y[d] = w[d] * x[d] / sqrt(mean_d x[d]^2 + eps). */
+void ora_rmsnorm_row(const double* x, int D, double eps, const double* w, double* y) {
+  double ss = 0.0;
+  for (int d = 0; d < D; ++d) ss += x[d] * x[d];
+  const double inv = 1.0 / sqrt(ss / (double)D + eps);
+  for (int d = 0; d < D; ++d) y[d] = w[d] * (x[d] * inv);
+}
+
+/* Rotary embedding on the first `rot` dims of a head row (rot even, 2 <= rot <= D),
+ * rotate-half within them: dim i < rot/2 pairs with dim i + rot/2 at angle
+ * theta_i = p * base^(-2i/rot); dims rot .. D-1 pass through unchanged.          */
+void ora_rope_row_partial(const double* x, int D, int rot, long p, double base, double* y) {
+  int h = rot / 2;
+  for (int d = rot; d < D; ++d) y[d] = x[d];
+  for (int i = 0; i < h; ++i) {
+    double th = (double)p * pow(base, -2.0 * (double)i / (double)rot);
+    double c = cos(th), s = sin(th);
+    y[i] = x[i] * c - x[h + i] * s;
+    y[h + i] = x[h + i] * c + x[i] * s;
   }
 }
 
@@ -146,35 +175,64 @@ static void window_of(long p, int S, int window, int* j0, int* nk) {
   *nk = (int)(hi - lo + 1);
 }
 
-/* Prepare (DyT then RoPE) every row of one [S, D] slice with parameter set t. */
-static void prep_slice(const double* x, int S, int D, double alpha, const double* gamma, const double* beta,
-                       double base, double* tmp, double* y) {
+#define ORA_NORM_DYT 0
+#define ORA_NORM_RMS 1
+
+/* How the q/k rows are prepared: the normaliser (DyT with alpha, gamma, beta, or
+ * RMSNorm with eps and weight w) and the rotary width rot (D: every dim). */
+typedef struct {
+  int norm;
+  double eps;
+  int rot;
+} prep_mode;
+
+/* Prepare (normalise, then rotate) every row of one [S, D] slice with parameter set t. */
+static void prep_slice(const double* x, int S, int D, prep_mode m, double alpha, const double* gamma,
+                       const double* beta, const double* w, double base, double* tmp, double* y) {
   for (int p = 0; p < S; ++p) {
-    ora_dyt_row(x + (int64_t)p * D, D, alpha, gamma, beta, tmp);
-    ora_rope_row(tmp, D, p, base, y + (int64_t)p * D);
+    if (m.norm == ORA_NORM_RMS)
+      ora_rmsnorm_row(x + (int64_t)p * D, D, m.eps, w, tmp);
+    else
+      ora_dyt_row(x + (int64_t)p * D, D, alpha, gamma, beta, tmp);
+    if (m.rot == D)
+      ora_rope_row(tmp, D, p, base, y + (int64_t)p * D);
+    else
+      ora_rope_row_partial(tmp, D, m.rot, p, base, y + (int64_t)p * D);
   }
 }
 
-/* Differential attention.  Inputs q1,k1,q2,k2,v [B,H,S,D]; out [B,H,S,D].
- * params: alpha[4], gamma[4*D], beta[4*D] (set t = 0:q1, 1:k1, 2:q2, 3:k2),
- * lam[H].  For each (b, h, p):
- *   qt = RoPE_p(DyT_t(q_t[p])), kt = RoPE_j(DyT_t(k_t[j]))           (t = q1,k1 / q2,k2)
- *   O_r = softmax_{j in W(p)}(scale <q_r, k_r,j>) . V[j]               (r = 1, 2)
+/* Differential attention, general form.  Inputs q1,k1,q2,k2,v [B,H,S,D]; out
+ * [B,H,S,D].  Normaliser: norm = ORA_NORM_DYT with alpha[4], gamma[4*D], beta[4*D],
+ * or ORA_NORM_RMS with eps and rms_w[4*D] (set t = 0:q1, 1:k1, 2:q2, 3:k2); rotary
+ * width rot (D, or an even width below it); lam[H]; v_keep [B*S] or NULL (all kept).
+ * For each (b, h, p):
+ *   qt = RoPE_p(Norm_t(q_t[p])), kt = RoPE_j(Norm_t(k_t[j]))         (t = q1,k1 / q2,k2)
+ *   O_r = softmax_{j in W(p)}(scale <q_r, k_r,j>) . V'[j]              (r = 1, 2)
+ *   V'[j] = V[j] if v_keep[b*S + j] != 0, else 0 (key j stays in the softmax)
  *   out = O_1 - lam[h] * O_2
  * rows as in ora_attn (flat index (b*H + h)*S + p).                                  */
-int ora_diffattn(const double* q1, const double* k1, const double* q2, const double* k2, const double* v,
-                 double* out, int B, int H, int S, int D, double scale, int window, const double* alpha,
-                 const double* gamma, const double* beta, double base, const double* lam, const int64_t* rows,
-                 int64_t nrows) {
-  if (!q1 || !k1 || !q2 || !k2 || !v || !out || !alpha || !gamma || !beta || !lam) return ORA_EBADARG;
-  if (B < 1 || H < 1 || S < 1 || D < 2 || (D % 2)) return ORA_EBADARG;
+int ora_diffattn_ex(const double* q1, const double* k1, const double* q2, const double* k2, const double* v,
+                    double* out, int B, int H, int S, int D, double scale, int window, int norm, const double* alpha,
+                    const double* gamma, const double* beta, double eps, const double* rms_w, int rot, double base,
+                    const double* lam, const unsigned char* v_keep, const int64_t* rows, int64_t nrows) {
+  if (!q1 || !k1 || !q2 || !k2 || !v || !out || !lam) return ORA_EBADARG;
+  if (norm == ORA_NORM_DYT && (!alpha || !gamma || !beta)) return ORA_EBADARG;
+  if (norm == ORA_NORM_RMS && (!rms_w || !(eps >= 0.0))) return ORA_EBADARG;
+  if (norm != ORA_NORM_DYT && norm != ORA_NORM_RMS) return ORA_EBADARG;
+  if (B < 1 || H < 1 || S < 1 || D < 2 || (D % 2) || rot < 2 || rot > D || (rot % 2)) return ORA_EBADARG;
   const double* src[4] = {q1, k1, q2, k2};
+  const prep_mode mode = {norm, eps, rot};
   int64_t plane = (int64_t)S * D;
   int err = 0;
+  double* zero_row = (double*)calloc((size_t)D, sizeof(double));
+  if (!zero_row) return ORA_ENOMEM;
   /* one (b, h) slice at a time: prepare all four tensors of the slice, then attend
    * the requested rows of that slice. */
   double* prep = (double*)malloc(sizeof(double) * 4 * plane);
-  if (!prep) return ORA_ENOMEM;
+  if (!prep) {
+    free(zero_row);
+    return ORA_ENOMEM;
+  }
   for (int64_t bh = 0; bh < (int64_t)B * H && !err; ++bh) {
     int h = (int)(bh % H);
     /* which rows of this slice are wanted */
@@ -191,7 +249,9 @@ int ora_diffattn(const double* q1, const double* k1, const double* q2, const dou
         err = ORA_ENOMEM;
         continue;
       }
-      prep_slice(src[t] + bh * plane, S, D, alpha[t], gamma + (int64_t)t * D, beta + (int64_t)t * D, base, tmp,
+      const int dyt = norm == ORA_NORM_DYT;
+      prep_slice(src[t] + bh * plane, S, D, mode, dyt ? alpha[t] : 0.0, dyt ? gamma + (int64_t)t * D : NULL,
+                 dyt ? beta + (int64_t)t * D : NULL, dyt ? NULL : rms_w + (int64_t)t * D, base, tmp,
                  prep + (int64_t)t * plane);
       free(tmp);
     }
@@ -201,6 +261,7 @@ int ora_diffattn(const double* q1, const double* k1, const double* q2, const dou
     const double* qh2 = prep + 2 * plane;
     const double* kh2 = prep + 3 * plane;
     const double* vb = v + bh * plane;
+    const unsigned char* keep = v_keep ? v_keep + (bh / H) * (int64_t)S : NULL;
     int64_t nr = rows ? nrows : S;
 #pragma omp parallel
     {
@@ -224,7 +285,7 @@ int ora_diffattn(const double* q1, const double* k1, const double* q2, const dou
           for (int j = 0; j < nk; ++j) {
             kr1[j] = kh1 + (int64_t)(j0 + j) * D;
             kr2[j] = kh2 + (int64_t)(j0 + j) * D;
-            vr[j] = vb + (int64_t)(j0 + j) * D;
+            vr[j] = (keep && !keep[j0 + j]) ? zero_row : vb + (int64_t)(j0 + j) * D;
           }
           attend_row(qh1 + p * D, kr1, vr, nk, D, scale, s, o1);
           attend_row(qh2 + p * D, kr2, vr, nk, D, scale, s, o2);
@@ -240,7 +301,18 @@ int ora_diffattn(const double* q1, const double* k1, const double* q2, const dou
     }
   }
   free(prep);
+  free(zero_row);
   return err;
+}
+
+/* Differential attention with DyT and rotary embedding over every dim, no V mask. */
+int ora_diffattn(const double* q1, const double* k1, const double* q2, const double* k2, const double* v,
+                 double* out, int B, int H, int S, int D, double scale, int window, const double* alpha,
+                 const double* gamma, const double* beta, double base, const double* lam, const int64_t* rows,
+                 int64_t nrows) {
+  if (!alpha || !gamma || !beta) return ORA_EBADARG;
+  return ora_diffattn_ex(q1, k1, q2, k2, v, out, B, H, S, D, scale, window, ORA_NORM_DYT, alpha, gamma, beta, 0.0,
+                         NULL, D, base, lam, NULL, rows, nrows);
 }
 
 /* Number of OpenMP threads the oracle will use (reported beside its timings). */

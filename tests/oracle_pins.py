@@ -17,7 +17,10 @@ builds) and raises AssertionError on failure.  The kinds of pin:
 Definitions follow "SDXL as a requirements inventory" s1.3 (softmax(q k^T/8) v per
 head) and "401 -> 163 ms: Stable Audio 3 medium on one TPU v6e chip" s3 / appendix
 E1-E2 (DyT, rotate-half rotary embedding, two softmax branches over a +-17 band
-masked by position, subtraction) with the readings stated in ka_oracle.c.
+masked by position, subtraction) with the readings stated in ka_oracle.c.  The
+same page's model forms (appendix D1, D3, D4, E1: per-head RMSNorm, rotary on 32
+of the 64 dims, V zeroed for padded tokens whose keys stay) are pinned against
+torch's rms_norm and SDPA, closed forms and a long-double brute force.
 """
 from __future__ import annotations
 
@@ -401,6 +404,146 @@ def pin_brute_force_long_double(ora):
     _close(out, ref, 1e-13, "diff brute force")
 
 
+# ------------------------------------------------------------------ model forms: RMSNorm, partial rotary, V mask
+
+def pin_rmsnorm_closed_forms(ora):
+    """A constant row c gives w c / sqrt(c^2 + eps); with eps = 0 and unit weights the output has mean
+    square exactly 1, is unchanged by positive scaling of x, and is odd in x."""
+    r = _rng(200)
+    w = r.uniform(0.5, 2.0, D)
+    for c in (0.3, -2.5, 7.0):
+        for eps in (0.0, 1e-6, 0.25):
+            _close(ora.rmsnorm_row(np.full(D, c), eps, w), w * c / np.sqrt(c * c + eps), 1e-15,
+                   f"rms constant c={c} eps={eps}")
+    x = r.standard_normal(D) * 3
+    y = ora.rmsnorm_row(x, 0.0, np.ones(D))
+    _close(np.mean(y * y), 1.0, 1e-15, "rms unit mean square")
+    _close(ora.rmsnorm_row(5.5 * x, 0.0, w), ora.rmsnorm_row(x, 0.0, w), 1e-15, "rms scale invariance")
+    _close(ora.rmsnorm_row(-x, 1e-3, w), -ora.rmsnorm_row(x, 1e-3, w), 0.0, "rms odd")
+
+
+def pin_rope_partial_basis_vectors(ora):
+    """Width 32: e_i -> cos t e_i + sin t e_{i+16}, e_{i+16} -> -sin t e_i + cos t e_{i+16} with
+    t = p base^(-2i/32); e_d for d >= 32 passes through.  Width 64 is the full rotation."""
+    for p in (0, 1, 7, 23085):
+        for i in (0, 1, 9, 15):
+            t = p * 10000.0 ** (-2.0 * i / 32.0)
+            e = np.zeros(D)
+            e[i] = 1.0
+            ref = np.zeros(D)
+            ref[i], ref[i + 16] = np.cos(t), np.sin(t)
+            _close(ora.rope_row_partial(e, 32, p, 10000.0), ref, 1e-13, f"rope32 e_{i} p={p}")
+            e = np.zeros(D)
+            e[i + 16] = 1.0
+            ref = np.zeros(D)
+            ref[i], ref[i + 16] = -np.sin(t), np.cos(t)
+            _close(ora.rope_row_partial(e, 32, p, 10000.0), ref, 1e-13, f"rope32 e_{i + 16} p={p}")
+        for d in (32, 41, 63):
+            e = np.zeros(D)
+            e[d] = 1.0
+            _close(ora.rope_row_partial(e, 32, p, 10000.0), e, 0.0, f"rope32 pass-through e_{d} p={p}")
+    x = _rng(201).standard_normal(D)
+    for p in (0, 3, 999):
+        _close(ora.rope_row_partial(x, 64, p, 10000.0), ora.rope_row(x, p, 10000.0), 1e-15, "rope width 64")
+
+
+def _torch_diff_model(q1, k1, q2, k2, v, scale, window, w, eps, base, lam, keep):
+    """The model form through torch: rms_norm (a library routine), complex rotation of pairs (i, i+16)
+    for i < 16 with dims 32..63 appended unrotated, SDPA with a boolean band mask, V times the flags."""
+    B, H, S, _ = q1.shape
+    pos = torch.arange(S, dtype=torch.float64)
+    freq = float(base) ** (-torch.arange(16, dtype=torch.float64) / 16.0)
+    rot = torch.polar(torch.ones(S, 16, dtype=torch.float64), pos[:, None] * freq[None, :])
+
+    def prep(x, t):
+        y = torch.nn.functional.rms_norm(torch.from_numpy(x), (D,), weight=torch.from_numpy(w[t]), eps=eps)
+        z = torch.complex(y[..., :16], y[..., 16:32]) * rot
+        return torch.cat([z.real, z.imag, y[..., 32:]], dim=-1).contiguous()
+
+    mask = None
+    if window >= 0:
+        idx = torch.arange(S)
+        mask = (idx[:, None] - idx[None, :]).abs() <= window
+    vt = (torch.from_numpy(v) * torch.from_numpy(keep.astype(np.float64))[:, None, :, None]).contiguous()
+    o1 = torch.nn.functional.scaled_dot_product_attention(prep(q1, 0), prep(k1, 1), vt, attn_mask=mask, scale=scale)
+    o2 = torch.nn.functional.scaled_dot_product_attention(prep(q2, 2), prep(k2, 3), vt, attn_mask=mask, scale=scale)
+    return (o1 - torch.from_numpy(lam)[None, :, None, None] * o2).numpy()
+
+
+def _model_params(H, seed):
+    r = _rng(seed)
+    return r.uniform(0.5, 2.0, (4, D)), r.uniform(0.2, 0.9, H)
+
+
+def pin_diff_model_form_vs_torch(ora):
+    for (B, H, S, win, eps, seed) in [(1, 2, 40, 5, 1e-6, 210), (2, 1, 33, -1, 1e-5, 211), (1, 3, 64, 17, 0.1, 212)]:
+        q1, k1, q2, k2, v = _diff_inputs(B, H, S, seed, qk_scale=2.0)
+        w, lm = _model_params(H, seed + 1)
+        keep = (_rng(seed + 2).random((B, S)) > 0.25).astype(np.uint8)
+        out = ora.diffattn(q1, k1, q2, k2, v, 0.125, win, None, None, None, 10000.0, lm, norm="rms", rms_weight=w,
+                           rms_eps=eps, rotary_dims=32, v_keep=keep)
+        ref = _torch_diff_model(q1, k1, q2, k2, v, 0.125, win, w, eps, 10000.0, lm, keep)
+        _close(out, ref, 1e-11, f"model form vs torch S={S} w={win}")
+
+
+def pin_v_keep_semantics(ora):
+    """All flags set is the unmasked result bit for bit; none set gives exactly 0.  With one-hot V the
+    columns of kept tokens equal the unmasked output (masked keys stay in the softmax, so the kept
+    weights do not change) and the columns of padded tokens are exactly 0.  Flags index (b, token)."""
+    S, win = 40, 6
+    q1, k1, q2, k2, _ = _diff_inputs(2, 1, S, 220)
+    v = np.zeros((2, 1, S, D))
+    v[:, 0, np.arange(S), np.arange(S)] = 1.0  # key j -> column j (S <= D)
+    a, g, b, lm = _params(1, 221)
+    base = ora.diffattn(q1, k1, q2, k2, v, 0.125, win, a, g, b, 10000.0, lm)
+    ones = np.ones((2, S), dtype=np.uint8)
+    assert np.array_equal(ora.diffattn(q1, k1, q2, k2, v, 0.125, win, a, g, b, 10000.0, lm, v_keep=ones), base)
+    assert np.all(ora.diffattn(q1, k1, q2, k2, v, 0.125, win, a, g, b, 10000.0, lm, v_keep=0 * ones) == 0.0)
+    keep = (_rng(222).random((2, S)) > 0.4).astype(np.uint8)
+    keep[0, :5] = 0
+    keep[1, :5] = 1  # the two batches differ
+    out = ora.diffattn(q1, k1, q2, k2, v, 0.125, win, a, g, b, 10000.0, lm, v_keep=keep)
+    for bb in range(2):
+        kept = keep[bb].astype(bool)
+        _close(out[bb, 0][:, :S][:, kept], base[bb, 0][:, :S][:, kept], 1e-15, f"kept columns b={bb}")
+        assert np.all(out[bb, 0][:, :S][:, ~kept] == 0.0), f"padded columns b={bb}"
+    for win2 in (-1, 3):
+        one = ora.diffattn(q1[1:], k1[1:], q2[1:], k2[1:], v[1:], 0.125, win2, a, g, b, 10000.0, lm, v_keep=keep[1:])
+        both = ora.diffattn(q1, k1, q2, k2, v, 0.125, win2, a, g, b, 10000.0, lm, v_keep=keep)
+        assert np.array_equal(both[1:], one), f"flags follow the batch index (w={win2})"
+
+
+def pin_brute_force_model_form(ora):
+    """Long-double brute force of the model form on a tiny input: RMSNorm, a 2x2 rotation per pair
+    (i, i+16) for i < 16, dims 32..63 untouched, V rows of padded tokens zero, band mask."""
+    S, win, eps = 7, 2, 1e-3
+    q1, k1, q2, k2, v = (t[0, 0] for t in _diff_inputs(1, 1, S, 230, qk_scale=2.0))
+    w, lm = _model_params(1, 231)
+    keep = np.array([1, 0, 1, 1, 0, 1, 1], dtype=np.uint8)
+
+    def prep(x, t, p):
+        x = np.asarray(x, dtype=np.longdouble)
+        y = w[t].astype(np.longdouble) * x / np.sqrt(np.mean(x * x) + np.longdouble(eps))
+        out = y.copy()
+        for i in range(16):
+            th = np.longdouble(p) * np.longdouble(10000.0) ** (-np.longdouble(2 * i) / 32)
+            m = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]], dtype=np.longdouble)
+            out[i], out[i + 16] = m @ np.array([y[i], y[i + 16]], dtype=np.longdouble)
+        return out
+
+    mask = np.abs(np.arange(S)[:, None] - np.arange(S)[None, :]) <= win
+    vk = v * keep[:, None]
+    o1 = _ld_attn(np.stack([prep(q1[p], 0, p) for p in range(S)]), np.stack([prep(k1[j], 1, j) for j in range(S)]),
+                  vk, 0.125, mask)
+    o2 = _ld_attn(np.stack([prep(q2[p], 2, p) for p in range(S)]), np.stack([prep(k2[j], 3, j) for j in range(S)]),
+                  vk, 0.125, mask)
+    ref = (o1 - np.longdouble(lm[0]) * o2).astype(np.float64)
+    out = ora.diffattn(q1[None, None], k1[None, None], q2[None, None], k2[None, None], v[None, None], 0.125, win,
+                       None, None, None, 10000.0, lm, norm="rms", rms_weight=w, rms_eps=eps, rotary_dims=32,
+                       v_keep=keep[None])[0, 0]
+    _close(out, ref, 1e-13, "model form brute force")
+
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_") and callable(obj)]
 
 
@@ -412,4 +555,6 @@ def bound_oracle(lib):
     ns.diffattn = lambda *a, **kw: oracle.diffattn(*a, lib=lib, **kw)
     ns.dyt_row = lambda *a, **kw: oracle.dyt_row(*a, lib=lib, **kw)
     ns.rope_row = lambda *a, **kw: oracle.rope_row(*a, lib=lib, **kw)
+    ns.rmsnorm_row = lambda *a, **kw: oracle.rmsnorm_row(*a, lib=lib, **kw)
+    ns.rope_row_partial = lambda *a, **kw: oracle.rope_row_partial(*a, lib=lib, **kw)
     return ns

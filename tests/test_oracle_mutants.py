@@ -37,8 +37,23 @@ MUTANTS = {
     "lambda_wrong_head": ("out[flat * D + d] = o1[d] - lam[h] * o2[d];", "out[flat * D + d] = o1[d] - lam[0] * o2[d];"),
     "branch2_uses_branch1_keys": ("attend_row(qh2 + p * D, kr2, vr, nk", "attend_row(qh2 + p * D, kr1, vr, nk"),
     "branch2_uses_branch1_query": ("attend_row(qh2 + p * D, kr2", "attend_row(qh1 + p * D, kr2"),
-    "one_param_set_for_all": ("prep_slice(src[t] + bh * plane, S, D, alpha[t], gamma + (int64_t)t * D, beta + (int64_t)t * D",
-                              "prep_slice(src[t] + bh * plane, S, D, alpha[0], gamma, beta"),
+    "one_param_set_for_all": ("dyt ? alpha[t] : 0.0, dyt ? gamma + (int64_t)t * D : NULL,\n"
+                              "                 dyt ? beta + (int64_t)t * D : NULL",
+                              "dyt ? alpha[0] : 0.0, dyt ? gamma : NULL,\n                 dyt ? beta : NULL"),
+    "rms_drops_eps": ("1.0 / sqrt(ss / (double)D + eps);", "1.0 / sqrt(ss / (double)D);"),
+    "rms_sum_not_mean": ("1.0 / sqrt(ss / (double)D + eps);", "1.0 / sqrt(ss + eps);"),
+    "rms_eps_outside_root": ("1.0 / sqrt(ss / (double)D + eps);", "1.0 / (sqrt(ss / (double)D) + eps);"),
+    "rms_drops_weight": ("y[d] = w[d] * (x[d] * inv);", "y[d] = x[d] * inv;"),
+    "rms_one_weight_set": ("dyt ? NULL : rms_w + (int64_t)t * D", "dyt ? NULL : rms_w"),
+    "rope_partial_sign": ("y[i] = x[i] * c - x[h + i] * s;", "y[i] = x[i] * c + x[h + i] * s;"),
+    "rope_partial_pairs_half_head": ("y[i] = x[i] * c - x[h + i] * s;\n    y[h + i] = x[h + i] * c + x[i] * s;",
+                                     "y[i] = x[i] * c - x[D / 2 + i] * s;\n    y[D / 2 + i] = x[D / 2 + i] * c + x[i] * s;"),
+    "rope_partial_frequency_over_head": ("-2.0 * (double)i / (double)rot", "-2.0 * (double)i / (double)D"),
+    "rope_partial_tail_dropped": ("for (int d = rot; d < D; ++d) y[d] = x[d];", "for (int d = rot; d < D; ++d) y[d] = 0.0;"),
+    "rope_width_ignored": ("if (m.rot == D)", "if (1)"),
+    "v_keep_ignored": ("vr[j] = (keep && !keep[j0 + j]) ? zero_row : vb", "vr[j] = vb"),
+    "v_keep_inverted": ("vr[j] = (keep && !keep[j0 + j]) ? zero_row : vb", "vr[j] = (keep && keep[j0 + j]) ? zero_row : vb"),
+    "v_keep_wrong_batch": ("v_keep + (bh / H) * (int64_t)S", "v_keep + (bh % H) * (int64_t)S"),
     "rope_position_ignored": ("ora_rope_row(tmp, D, p, base, y + (int64_t)p * D);",
                               "ora_rope_row(tmp, D, 0, base, y + (int64_t)p * D);"),
     "dense_wrong_head_kv": ("int64_t bh = flat / Sq;", "int64_t bh = (flat / Sq) % (B * H > 1 ? B * H - 1 : 1);"),
