@@ -157,7 +157,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--forms", default="cross,band,full", help="extra forms to time (comma list, or 'none')")
+    ap.add_argument("--forms", default="cross,band,full,band_model,full_model",
+                    help="extra forms to time (comma list, or 'none')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -263,6 +264,50 @@ def main():
                               "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
                               "GB/s": round(b / sec / 1e9, 1), "bound": "mfma", "flops": f, "bytes": b}
         log(f"bench: full {forms['full_diff']}")
+    # ---------------- the model forms: decoder (DyT, 32 rotary dims), DiT (RMSNorm, 32 rotary dims, padded V)
+    if "band_model" in wanted:
+        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
+        log(f"bench: {wl.desc}, decoder form (DyT, 32 rotary dims)")
+        sets = []
+        for s_ in range(3):
+            ins, prm = synth.make_diff(wl, seed_base=1000 * wl.index + 10 * s_)
+            sets.append(([up(x, torch) for x in ins], [up(x, torch) for x in prm]))
+        outs = [torch.empty_like(s_[0][0]) for s_ in sets]
+        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
+
+        def band_model(i):
+            ins, (a_, g_, b_, l_) = sets[i]
+            ka.ka_diffattn_fwd_ex(*ins, l_, o=outs[i], scale=wl.scale, window=wl.window, qk_norm="dyt", alpha=a_,
+                                  gamma=g_, beta=b_, rotary_dims=32)
+
+        sec = time_graph(band_model, len(sets), args.steps, args.warmup, torch)
+        forms["band_diff_model"] = {"workload": wl.key, "options": "DyT, rotary on 32 of 64 dims",
+                                    "kernel": "diff_band", "us": round(sec * 1e6, 3), "GB/s": round(b / sec / 1e9, 1),
+                                    "hbm_frac": round(b / sec / acc.HBM_PEAK, 4), "bound": "hbm", "bytes": b,
+                                    "input_copies": len(sets)}
+        log(f"bench: band model form {forms['band_diff_model']}")
+        del sets, outs
+    if "full_model" in wanted:
+        wl = synth.WORKLOADS["sa3_dit_fulldiff_h16s1422"]
+        pad = 142
+        log(f"bench: {wl.desc}, DiT form (RMSNorm, 32 rotary dims, last {pad} tokens padded)")
+        ins, _ = synth.make_diff(wl)
+        ins = [up(x, torch) for x in ins]
+        w_, l_ = (up(x, torch) for x in synth.make_model_params(wl.H, 1000 * wl.index + 6))
+        keep = up(synth.make_v_keep(wl.B, wl.Sq, pad), torch)
+        o = torch.empty_like(ins[0])
+        ws = torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
+                         device="cuda")
+        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
+        sec = time_graph(lambda i: ka.ka_diffattn_fwd_ex(*ins, l_, o=o, scale=wl.scale, window=wl.window,
+                                                         qk_norm="rms", rms_weight=w_, rms_eps=1e-6, rotary_dims=32,
+                                                         v_keep=keep, workspace=ws),
+                         1, args.steps, args.warmup, torch)
+        forms["full_diff_model"] = {"workload": wl.key, "options": f"RMSNorm, rotary on 32 of 64 dims, {pad} padded",
+                                    "kernel": "diff_kprep + diff_flash", "us": round(sec * 1e6, 3),
+                                    "TFLOP/s": round(f / sec / 1e12, 3),
+                                    "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4), "bound": "mfma", "flops": f}
+        log(f"bench: full model form {forms['full_diff_model']}")
     if forms:
         result["forms"] = forms
 

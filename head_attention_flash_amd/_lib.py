@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(PKG, "libka_attn.so")
 KA_OK, KA_ERR_NULL, KA_ERR_SHAPE, KA_ERR_UNSUPPORTED, KA_ERR_PARAM, KA_ERR_ALIGN, KA_ERR_ALIAS, \
     KA_ERR_WORKSPACE, KA_ERR_HIP = range(9)
 KA_F32, KA_BF16 = 0, 1
+KA_QKNORM_DYT, KA_QKNORM_RMS = 0, 1
 KA_XATTN_MAX_SK = 256
 
 # every symbol include/ka_attn.h declares
-EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_workspace_bytes", "ka_status_string",
-           "ka_last_hip_error", "ka_version")
+EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_fwd_ex", "ka_diffattn_workspace_bytes",
+           "ka_status_string", "ka_last_hip_error", "ka_version")
 
 
 class KaError(RuntimeError):
@@ -51,6 +52,9 @@ def load(path: str = LIB_PATH):
     lib.ka_xattn_fwd.restype = i
     lib.ka_diffattn_fwd.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, f, vp, vp, sz, vp]
     lib.ka_diffattn_fwd.restype = i
+    lib.ka_diffattn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, vp, vp, f, i, f, vp,
+                                       vp, vp, sz, vp]
+    lib.ka_diffattn_fwd_ex.restype = i
     lib.ka_diffattn_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.ka_diffattn_workspace_bytes.restype = sz
     lib.ka_status_string.argtypes = [i]
@@ -150,4 +154,33 @@ def ka_diffattn_fwd(q1, k1, q2, k2, v, alpha, gamma, beta, lam, o=None, scale: f
                              _dev(alpha, "alpha"), _dev(gamma, "gamma"), _dev(beta, "beta"), float(rope_base),
                              _dev(lam, "lambda"), ws_ptr, ws_bytes, _stream(stream))
     _check(lib, st, "ka_diffattn_fwd")
+    return o
+
+
+def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, window: int = -1, qk_norm: str = "dyt",
+                       alpha=None, gamma=None, beta=None, rms_weight=None, rms_eps: float = 1e-6,
+                       rotary_dims: int = 64, rope_base: float = 10000.0, v_keep=None, workspace=None, stream=None):
+    """Differential attention (bf16) in the model forms: qk_norm "dyt" (alpha [4], gamma/beta [4,64]) or
+    "rms" (rms_weight [4,64], rms_eps); rotary_dims 64 or 32; v_keep: optional [B,S] uint8 GPU tensor
+    (0 = that token's V row is zero, its key stays).  All parameter tensors are fp32 GPU tensors.
+    """
+    lib = load()
+    B, H, S, D = q1.shape
+    if o is None:
+        o = _torch().empty_like(q1)
+    need = int(lib.ka_diffattn_workspace_bytes(B, H, S, D, window))
+    if workspace is None and need:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q1.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    norm = {"dyt": KA_QKNORM_DYT, "rms": KA_QKNORM_RMS}[qk_norm]
+    opt = lambda t, name: _dev(t, name) if t is not None else ctypes.c_void_p(0)  # noqa: E731
+    if v_keep is not None and v_keep.dtype != _torch().uint8:
+        raise TypeError("v_keep must be a uint8 tensor")
+    st = lib.ka_diffattn_fwd_ex(_dtype_code(q1), _dev(q1, "q1"), _dev(k1, "k1"), _dev(q2, "q2"), _dev(k2, "k2"),
+                                _dev(v, "v"), _dev(o, "o"), B, H, S, S, D, float(scale), int(window), norm,
+                                opt(alpha, "alpha"), opt(gamma, "gamma"), opt(beta, "beta"),
+                                opt(rms_weight, "rms_weight"), float(rms_eps), int(rotary_dims), float(rope_base),
+                                _dev(lam, "lambda"), opt(v_keep, "v_keep"), ws_ptr, ws_bytes, _stream(stream))
+    _check(lib, st, "ka_diffattn_fwd_ex")
     return o

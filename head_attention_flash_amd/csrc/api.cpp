@@ -91,18 +91,25 @@ ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void*
 size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window) {
   size_t n = 0;
   if (B < 1 || H < 1 || S < 1 || D != 64 || !tensor_bytes(B, H, S, D, 2, &n)) return 0;
-  return ka::diff_workspace_bytes(B, H, S, window);
+  return ka::diff_workspace_bytes(B, H, S, window, true);  // enough with or without V flags
 }
 
-ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
-                          const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
-                          const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta, float rope_base,
-                          const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!q1 || !k1 || !q2 || !k2 || !v || !o || !dyt_alpha || !dyt_gamma || !dyt_beta || !lambda) return KA_ERR_NULL;
+ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                             const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                             ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
+                             const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
+                             float rope_base, const float* lambda, const uint8_t* v_keep, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (qk_norm != KA_QKNORM_DYT && qk_norm != KA_QKNORM_RMS) return KA_ERR_UNSUPPORTED;
+  if (!q1 || !k1 || !q2 || !k2 || !v || !o || !lambda) return KA_ERR_NULL;
+  if (qk_norm == KA_QKNORM_DYT && (!dyt_alpha || !dyt_gamma || !dyt_beta)) return KA_ERR_NULL;
+  if (qk_norm == KA_QKNORM_RMS && !rms_weight) return KA_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || Sq != Sk) return KA_ERR_SHAPE;
   if (D != 64 || dtype != KA_BF16) return KA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(rope_base) || !(rope_base > 1.0f))
     return KA_ERR_PARAM;
+  if (rotary_dims != 32 && rotary_dims != 64) return KA_ERR_PARAM;
+  if (qk_norm == KA_QKNORM_RMS && (!std::isfinite(rms_eps) || !(rms_eps > 0.0f))) return KA_ERR_PARAM;
   const int S = Sq;
   size_t tb = 0;
   if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
@@ -111,7 +118,7 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   for (const void* p : ins)
     if (!aligned16(p)) return KA_ERR_ALIGN;
   if (!aligned16(o)) return KA_ERR_ALIGN;
-  const size_t need = ka::diff_workspace_bytes(B, H, S, window);
+  const size_t need = ka::diff_workspace_bytes(B, H, S, window, v_keep != nullptr);
   if (need) {
     if (!workspace) return KA_ERR_NULL;
     if (workspace_bytes < need) return KA_ERR_WORKSPACE;
@@ -123,6 +130,10 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   if (need)
     for (const void* p : ins)
       if (overlap(workspace, need, p, tb)) return KA_ERR_ALIAS;
+  if (v_keep) {
+    const size_t nk = (size_t)B * S;
+    if (overlap(o, tb, v_keep, nk) || (need && overlap(workspace, need, v_keep, nk))) return KA_ERR_ALIAS;
+  }
 
   ka::DiffArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -136,7 +147,12 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   a.alpha = dyt_alpha;
   a.gamma = dyt_gamma;
   a.beta = dyt_beta;
+  a.rms_w = rms_weight;
   a.lambda = lambda;
+  a.v_keep = v_keep;
+  a.norm = qk_norm == KA_QKNORM_RMS ? 1 : 0;
+  a.rms_eps = rms_eps;
+  a.rot32 = rotary_dims == 32;
   a.B = B;
   a.H = H;
   a.S = S;
@@ -148,17 +164,31 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   int pbits = 1;
   while ((1 << pbits) < S) ++pbits;
   a.split_angles = pbits <= 16;
+  // pair i: 64 rotary dims pair (i, i+32) for i < 32; 32 rotary dims pair (i, i+16) for
+  // i < 16 at base^(-2i/32), and the threads' pairs 16..31 hold unrotated dims (angle 0)
   for (int i = 0; i < 32; ++i) {
-    const double r = std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi;
+    const double r = rotary_dims == 64 ? std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi
+                     : i < 16         ? std::pow((double)rope_base, -2.0 * i / 32.0) / two_pi
+                                      : 0.0;
     a.rev[i] = r;
     int ex = 0;
-    std::frexp(r, &ex);                                // r = m * 2^ex, 0.5 <= m < 1
+    std::frexp(r, &ex);                                // r = m * 2^ex, 0.5 <= m < 1 (r = 0: 0)
     const double q = std::ldexp(1.0, ex - (24 - pbits));
     const double hi = std::round(r / q) * q;           // 24 - pbits significant bits
     a.rev_hi[i] = (float)hi;
     a.rev_lo[i] = (float)(r - hi);
   }
   return hip_status(ka::launch_diffattn(a, stream));
+}
+
+ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                          const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                          const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta, float rope_base,
+                          const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dyt_alpha || !dyt_gamma || !dyt_beta) return KA_ERR_NULL;
+  return ka_diffattn_fwd_ex(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, KA_QKNORM_DYT, dyt_alpha,
+                            dyt_gamma, dyt_beta, nullptr, 1.0f, 64, rope_base, lambda, nullptr, workspace,
+                            workspace_bytes, stream);
 }
 
 const char* ka_status_string(ka_status s) {

@@ -14,6 +14,14 @@
 // beta) set per tensor q1, k1, q2, k2; rotary over all 64 dims, pairs (i, i+32),
 // theta_i = p base^(-2i/64), p = token index; o = O_1 - lambda[h] O_2.
 //
+// The Stable Audio 3 model's own forms (appendix D1, D3, D4, E1), selected per call:
+// per-head RMSNorm in place of DyT, x~ = w[d] x / sqrt(mean x^2 + eps); rotary on
+// dims 0..31 only (rotate-half pairs i, i+16 at theta_i = p base^(-2i/32), dims
+// 32..63 pass through); and V rows of padded tokens taken as zero while their keys
+// stay in both softmaxes.  With the 32-dim rotary a thread loads dims (8c, 8c+16)
+// for c < 2 and (8c+16, 8c+32) for c >= 2 and stores them where (8c, 8c+32) go
+// otherwise: q^ and k^ are held in one common dim order, which leaves q^ . k^ as it is.
+//
 // Precision plan: DyT, rotation, softmax and subtraction in fp32; the rotated
 // q^/k^ (bounded by |gamma| + |beta|) enter Q K^T as fp16 (8x finer than bf16;
 // the TPU kernel's bf16 q/k moves near-argmax scores by ~1e-2); P enters P.V as
@@ -29,7 +37,8 @@
 //   diff_kprep         full (or wide-window) path, pass 1: DyT + rotation of K1 and
 //                      K2, once per (b, h) and key -- never once per query block
 //                      (V1 / Session 8: re-preparing K per query block was half the
-//                      kernel's vector work) -- into the fp16 workspace.
+//                      kernel's vector work) -- into the fp16 workspace; with V
+//                      flags also V with the flagged-out rows zeroed.
 //   diff_flash<..>     pass 2: q prep in registers, then a pipelined two-branch
 //                      flash loop over 64-key tiles of the prepared keys and V.
 #include <type_traits>
@@ -46,32 +55,59 @@ struct SharedParams {
   double rev[32];        // revolutions per position, pair i (fp64 angle path)
   float rev_hi[32];      // split fp32 angle path
   float rev_lo[32];
-  float gpb[4][HD];      // DyT gamma + beta per set (q1, k1, q2, k2)
+  float gpb[4][HD];      // DyT gamma + beta per set (q1, k1, q2, k2); RMSNorm: the weight
   float m2g[4][HD];      // DyT -2 gamma per set
   float k2a[4];          // 2 log2(e) alpha per set
+  float eps;             // RMSNorm
   int split;
 };
 
+constexpr int NORM_DYT = 0, NORM_RMS = 1;
+
+template <int NORM>
 __device__ __forceinline__ void load_params(SharedParams& sp, const DiffArgs& a) {
   for (int i = threadIdx.x; i < 4 * HD; i += blockDim.x) {
-    const float g = a.gamma[i], b = a.beta[i];
-    sp.gpb[i / HD][i % HD] = g + b;
-    sp.m2g[i / HD][i % HD] = -2.0f * g;
+    if constexpr (NORM == NORM_RMS) {
+      sp.gpb[i / HD][i % HD] = a.rms_w[i];
+    } else {
+      const float g = a.gamma[i], b = a.beta[i];
+      sp.gpb[i / HD][i % HD] = g + b;
+      sp.m2g[i / HD][i % HD] = -2.0f * g;
+    }
   }
   if (threadIdx.x < 32) {
     sp.rev[threadIdx.x] = a.rev[threadIdx.x];
     sp.rev_hi[threadIdx.x] = a.rev_hi[threadIdx.x];
     sp.rev_lo[threadIdx.x] = a.rev_lo[threadIdx.x];
   }
-  if (threadIdx.x < 4) sp.k2a[threadIdx.x] = 2.0f * LOG2E * a.alpha[threadIdx.x];
-  if (threadIdx.x == 0) sp.split = a.split_angles;
+  if (NORM == NORM_DYT && threadIdx.x < 4) sp.k2a[threadIdx.x] = 2.0f * LOG2E * a.alpha[threadIdx.x];
+  if (threadIdx.x == 0) {
+    sp.split = a.split_angles;
+    sp.eps = a.rms_eps;
+  }
 }
 
-// DyT then rotation, for 8 rotary pairs (dims i0+e and i0+32+e) of two tensors
-// (parameter sets ta and tb) at the same position p; the angles are shared.
-__device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int i0, int p, int ta,
-                                            int tb, const SharedParams& sp) {
-  const float ka = sp.k2a[ta], kb = sp.k2a[tb];
+// The dims a thread with chunk index c (0..3) holds of a head row: 8 at lo_dim and
+// the 8 they pair with (or, past the rotary dims, the next 8 unrotated ones) at
+// lo_dim + pair_gap.  Rotary pair index 8c + e in both layouts.
+__device__ __forceinline__ int lo_dim(int c, bool rot32) { return rot32 && c >= 2 ? 8 * c + 16 : 8 * c; }
+__device__ __forceinline__ int pair_gap(bool rot32) { return rot32 ? 16 : 32; }
+
+// Lanes holding one head row: four consecutive lanes (RED_QUAD) or {l, l^16, l^32,
+// l^48} (RED_GROUP4).
+constexpr int RED_QUAD = 0, RED_GROUP4 = 1;
+template <int RED>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (RED == RED_QUAD) return quad_sum(x);
+  else return group4_sum(x);
+}
+
+// Normalise (DyT, or RMSNorm over the row's 64 dims held by four lanes), then rotate,
+// 8 rotary pairs (dims d0+e and d0+gap+e, pair index i0+e) of two tensors (parameter
+// sets ta and tb) at the same position p; the angles are shared.
+template <int NORM, int RED>
+__device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int d0, int gap, int i0,
+                                            int p, int ta, int tb, const SharedParams& sp) {
   const float pf = (float)p;
   // one uniform branch for all eight angles, so that the straight-line DyT and rotation
   // below form one block the scheduler can interleave
@@ -83,17 +119,31 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) rope_cs_f64(p, sp.rev[i0 + e], csv[e], snv[e]);
   }
+  float ra = 1.0f, rb = 1.0f;  // RMSNorm: 1 / sqrt(mean x^2 + eps) of each row
+  if constexpr (NORM == NORM_RMS) {
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sa = __builtin_fmaf(alo[e], alo[e], __builtin_fmaf(ahi[e], ahi[e], sa));
+      sb = __builtin_fmaf(blo[e], blo[e], __builtin_fmaf(bhi[e], bhi[e], sb));
+    }
+    ra = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sa), 1.0f / HD, sp.eps));
+    rb = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sb), 1.0f / HD, sp.eps));
+  }
+  const float ka = sp.k2a[ta], kb = sp.k2a[tb];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int i = i0 + e;
+    const int dl = d0 + e, dh = d0 + gap + e;
     const float cs = csv[e], sn = snv[e];
-    const float a0 = dyt(alo[e], ka, sp.gpb[ta][i], sp.m2g[ta][i]);
-    const float a1 = dyt(ahi[e], ka, sp.gpb[ta][i + 32], sp.m2g[ta][i + 32]);
+    auto norm = [&](float x, int t, int d, float k, float r) {
+      if constexpr (NORM == NORM_RMS) return sp.gpb[t][d] * (x * r);
+      else return dyt(x, k, sp.gpb[t][d], sp.m2g[t][d]);
+    };
+    const float a0 = norm(alo[e], ta, dl, ka, ra), a1 = norm(ahi[e], ta, dh, ka, ra);
     // explicit fused forms: every tensor rounds identically, whatever the compiler would contract
     alo[e] = __builtin_fmaf(a0, cs, -(a1 * sn));
     ahi[e] = __builtin_fmaf(a1, cs, a0 * sn);
-    const float b0 = dyt(blo[e], kb, sp.gpb[tb][i], sp.m2g[tb][i]);
-    const float b1 = dyt(bhi[e], kb, sp.gpb[tb][i + 32], sp.m2g[tb][i + 32]);
+    const float b0 = norm(blo[e], tb, dl, kb, rb), b1 = norm(bhi[e], tb, dh, kb, rb);
     blo[e] = __builtin_fmaf(b0, cs, -(b1 * sn));
     bhi[e] = __builtin_fmaf(b1, cs, b0 * sn);
   }
@@ -106,12 +156,12 @@ __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
   return r;
 }
 
-// Load dims [i0, i0+8) and [i0+32, i0+40) of one bf16 row as fp32 (zeros if !ok).
-__device__ __forceinline__ void load_pairs(const unsigned short* row, int i0, bool ok, float* lo, float* hi) {
+// Load dims [d0, d0+8) and [d0+gap, d0+gap+8) of one bf16 row as fp32 (zeros if !ok).
+__device__ __forceinline__ void load_pairs(const unsigned short* row, int d0, int gap, bool ok, float* lo, float* hi) {
   uint4 a = make_uint4(0, 0, 0, 0), b = a;
   if (ok) {
-    a = ld16(row + i0);
-    b = ld16(row + i0 + 32);
+    a = ld16(row + d0);
+    b = ld16(row + d0 + gap);
   }
   unpack_bf16x8(a, lo);
   unpack_bf16x8(b, hi);
@@ -132,42 +182,55 @@ constexpr int BAND_TARGET_WGS = 768;  // about three resident workgroups per CU
 #define BAND_WPE 3
 #endif
 
-// One thread's share of one new row: dims [8cc, 8cc+8) and [8cc+32, 8cc+40) of k1
-// and k2, and bytes [32cc, 32cc+32) of v.
+// One thread's share of one new row: dims [d0, d0+8) and [d0+gap, d0+gap+8) of k1
+// and k2 (d0 = lo_dim(cc)), bytes [32cc, 32cc+32) of v, and the row's V flag.
 struct RowStage {
   uint4 k1lo, k1hi, k2lo, k2hi, v0, v1;
+  unsigned vkeep;
 };
 
 // Rows j outside [0, S) read as zero through the buffer resources (a negative row
-// offset wraps past the end), so no lane branches.
+// offset wraps past the end), so no lane branches.  keep: the V flags of this batch
+// index ([S] bytes), read only when the call passes them.
 struct BandSrc {
-  rsrc_t k1, k2, v;
+  rsrc_t k1, k2, v, keep;
+  bool has_keep;
 };
-__device__ __forceinline__ void stage_load(RowStage& st, const BandSrc& src, int j, int cc) {
+__device__ __forceinline__ void stage_load(RowStage& st, const BandSrc& src, int j, int cc, int d0, int gap) {
   const int off = j * (HD * 2);
-  st.k1lo = buf_ld16(src.k1, off + 16 * cc);
-  st.k1hi = buf_ld16(src.k1, off + 64 + 16 * cc);
-  st.k2lo = buf_ld16(src.k2, off + 16 * cc);
-  st.k2hi = buf_ld16(src.k2, off + 64 + 16 * cc);
+  st.k1lo = buf_ld16(src.k1, off + 2 * d0);
+  st.k1hi = buf_ld16(src.k1, off + 2 * (d0 + gap));
+  st.k2lo = buf_ld16(src.k2, off + 2 * d0);
+  st.k2hi = buf_ld16(src.k2, off + 2 * (d0 + gap));
   st.v0 = buf_ld16(src.v, off + 32 * cc);
   st.v1 = buf_ld16(src.v, off + 32 * cc + 16);
+  // past either end the flag reads 0, and the V row there is zero anyway
+  st.vkeep = src.has_keep ? buf_ld1(src.keep, j) : 1u;
 }
 
+template <int NORM>
 __device__ __forceinline__ void stage_commit(const RowStage& st, unsigned short* K1s, unsigned short* K2s,
-                                             unsigned short* Vs, int slot, int j, int cc, const SharedParams& sp) {
+                                             unsigned short* Vs, int slot, int j, int cc, int d0, int gap,
+                                             bool has_keep, const SharedParams& sp) {
   float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
   unpack_bf16x8(st.k1lo, k1lo);
   unpack_bf16x8(st.k1hi, k1hi);
   unpack_bf16x8(st.k2lo, k2lo);
   unpack_bf16x8(st.k2hi, k2hi);
   // rows no query of the strip sees are prepared too (finite, and masked in every tile)
-  prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);
+  prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, sp);
   st16(&K1s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1lo)));
   st16(&K1s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1hi)));
   st16(&K2s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2lo)));
   st16(&K2s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2hi)));
-  st16(&Vs[slot * VPD + 16 * cc], st.v0);
-  st16(&Vs[slot * VPD + 16 * cc + 8], st.v1);
+  uint4 v0 = st.v0, v1 = st.v1;
+  if (has_keep) {  // uniform; a mask, not a select of two uint4 (which would put the stage in scratch)
+    const unsigned m = st.vkeep ? ~0u : 0u;
+    v0 = make_uint4(v0.x & m, v0.y & m, v0.z & m, v0.w & m);
+    v1 = make_uint4(v1.x & m, v1.y & m, v1.z & m, v1.w & m);
+  }
+  st16(&Vs[slot * VPD + 16 * cc], v0);
+  st16(&Vs[slot * VPD + 16 * cc + 8], v1);
 }
 
 // One branch of a 16-query tile against the 16*NKB-key slab starting at ring slot
@@ -233,7 +296,7 @@ __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsi
   l = L[0];
 }
 
-template <int NKB, int WPE>
+template <int NKB, int WPE, int NORM>
 __global__ __launch_bounds__(64 * BAND_NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void diff_band(DiffArgs a, int nblk) {
   constexpr int HALO = 8 * NKB - 8;       // slab of query tile q0 starts at key q0 - HALO
@@ -253,17 +316,21 @@ void diff_band(DiffArgs a, int nblk) {
   const int pos0 = strip0 - HALO;  // position held by ring slot 0
   // one (b, h) slice of each tensor; rows outside [0, S) read as zero
   const int rbytes = S * HD * 2;
-  const BandSrc src{make_rsrc(a.k1 + base, rbytes), make_rsrc(a.k2 + base, rbytes), make_rsrc(a.v + base, rbytes)};
+  const bool has_keep = a.v_keep != nullptr;
+  const BandSrc src{make_rsrc(a.k1 + base, rbytes), make_rsrc(a.k2 + base, rbytes), make_rsrc(a.v + base, rbytes),
+                    make_rsrc(has_keep ? static_cast<const void*>(a.v_keep + (bh / a.H) * (size_t)S) : a.v, S), has_keep};
   const rsrc_t q1rs = make_rsrc(a.q1 + base, rbytes), q2rs = make_rsrc(a.q2 + base, rbytes);
-  load_params(sp, a);
+  const bool rot32 = a.rot32 != 0;
+  const int gap = pair_gap(rot32), kd0 = lo_dim(cc, rot32), qd0 = lo_dim(grp, rot32);
+  load_params<NORM>(sp, a);
   __syncthreads();
 
   // fill the ring for the first block: positions pos0 .. pos0 + NR - 1
   for (int r = tid >> 2; r < NR; r += 64 * BAND_NW / 4) {
     const int j = pos0 + r;
     RowStage st;
-    stage_load(st, src, j, cc);
-    stage_commit(st, K1s, K2s, Vs, r, j, cc, sp);
+    stage_load(st, src, j, cc, kd0, gap);
+    stage_commit<NORM>(st, K1s, K2s, Vs, r, j, cc, kd0, gap, has_keep, sp);
   }
 
   // band mask by relative position: key j = q0 - HALO + 16kb + 4grp + e against
@@ -284,11 +351,11 @@ void diff_band(DiffArgs a, int nblk) {
   // queries of this wave for block 0
   uint4 qs[4];
   auto qload = [&](int r0) {
-    const int off = (r0 + 16 * w + col) * (HD * 2) + 16 * grp;  // rows past S read as zero
+    const int off = (r0 + 16 * w + col) * (HD * 2) + 2 * qd0;  // rows past S read as zero
     qs[0] = buf_ld16(q1rs, off);
-    qs[1] = buf_ld16(q1rs, off + 64);
+    qs[1] = buf_ld16(q1rs, off + 2 * gap);
     qs[2] = buf_ld16(q2rs, off);
-    qs[3] = buf_ld16(q2rs, off + 64);
+    qs[3] = buf_ld16(q2rs, off + 2 * gap);
   };
   qload(strip0);
   __syncthreads();
@@ -304,13 +371,13 @@ void diff_band(DiffArgs a, int nblk) {
     unpack_bf16x8(qs[1], q1hi);
     unpack_bf16x8(qs[2], q2lo);
     unpack_bf16x8(qs[3], q2hi);
-    prep_pairs2(q1lo, q1hi, q2lo, q2hi, 8 * grp, p, 0, 2, sp);
+    prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, sp);
     const f16x8 Q1[2] = {to_f16x8(q1lo), to_f16x8(q1hi)};
     const f16x8 Q2[2] = {to_f16x8(q2lo), to_f16x8(q2hi)};
     // fetch what the next block adds while this one computes
     const int jn = r0 + BAND_BM + HALO + (tid >> 2);
     RowStage st;
-    if (more) stage_load(st, src, jn, cc);
+    if (more) stage_load(st, src, jn, cc, kd0, gap);
     if (more) qload(r0 + BAND_BM);
 
     const int jbase = q0 - HALO;
@@ -333,32 +400,42 @@ void diff_band(DiffArgs a, int nblk) {
     }
     if (more) {
       __syncthreads();  // every wave is done with the rows about to be replaced
-      stage_commit(st, K1s, K2s, Vs, (jn - pos0) % NR, jn, cc, sp);
+      stage_commit<NORM>(st, K1s, K2s, Vs, (jn - pos0) % NR, jn, cc, kd0, gap, has_keep, sp);
       __syncthreads();
     }
   }
 }
 
 // ---------------------------------------------------------------- full path, pass 1: key prep
+template <int NORM>
 __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   __shared__ SharedParams sp;
-  load_params(sp, a);
+  load_params<NORM>(sp, a);
   __syncthreads();
   const size_t nrows = (size_t)a.B * a.H * a.S;
   const size_t row = (size_t)blockIdx.x * 64 + (threadIdx.x >> 2);
   const int cc = threadIdx.x & 3;
-  if (row >= nrows) return;
+  if (row >= nrows) return;  // whole quads: the four lanes of a row leave together
   const int j = (int)(row % (size_t)a.S);
+  const bool rot32 = a.rot32 != 0;
+  const int gap = pair_gap(rot32), d0 = lo_dim(cc, rot32);
   float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
-  load_pairs(a.k1 + row * HD, 8 * cc, true, k1lo, k1hi);
-  load_pairs(a.k2 + row * HD, 8 * cc, true, k2lo, k2hi);
-  prep_pairs2(k1lo, k1hi, k2lo, k2hi, 8 * cc, j, 1, 3, sp);
+  load_pairs(a.k1 + row * HD, d0, gap, true, k1lo, k1hi);
+  load_pairs(a.k2 + row * HD, d0, gap, true, k2lo, k2hi);
+  prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, sp);
   _Float16* w1 = a.ws + row * HD;
   _Float16* w2 = a.ws + nrows * HD + row * HD;
   st16(w1 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k1lo)));
   st16(w1 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k1hi)));
   st16(w2 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2lo)));
   st16(w2 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2hi)));
+  if (a.v_keep) {  // V with the rows of flagged-out tokens zeroed, for pass 2
+    const unsigned m = a.v_keep[(row / a.S / a.H) * a.S + j] != 0 ? ~0u : 0u;
+    unsigned short* w3 = reinterpret_cast<unsigned short*>(a.ws) + 2 * nrows * HD + row * HD;
+    const uint4 x0 = ld16(a.v + row * HD + 16 * cc), x1 = ld16(a.v + row * HD + 16 * cc + 8);
+    st16(w3 + 16 * cc, make_uint4(x0.x & m, x0.y & m, x0.z & m, x0.w & m));
+    st16(w3 + 16 * cc + 8, make_uint4(x1.x & m, x1.y & m, x1.z & m, x1.w & m));
+  }
 }
 
 constexpr int DBN = 64;  // keys per tile
@@ -467,7 +544,7 @@ __device__ __forceinline__ bool dpipe_softmax(f32x4 (&S)[4][NQB], int j0, int Sl
   return any;
 }
 
-template <int NQB, int NW, bool BAND>
+template <int NQB, int NW, bool BAND, int NORM>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void diff_flash(DiffArgs a) {
   __shared__ __align__(16) unsigned short K1b[2][DBN * KPD];
   __shared__ __align__(16) unsigned short K2b[2][DBN * KPD];
@@ -485,7 +562,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const size_t nrows = (size_t)a.B * a.H * S;
   const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
   const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
-  load_params(sp, a);
+  const bool rot32 = a.rot32 != 0;
+  const int gap = pair_gap(rot32), qd0 = lo_dim(grp, rot32);
+  load_params<NORM>(sp, a);
   __syncthreads();
 
   const int qblk0 = blockIdx.x * NW * 16 * NQB;
@@ -496,9 +575,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int p = q0 + 16 * i + col;
     float q1lo[8], q1hi[8], q2lo[8], q2hi[8];
     const size_t po = p < S ? (size_t)p * HD : 0;
-    load_pairs(a.q1 + base + po, 8 * grp, p < S, q1lo, q1hi);
-    load_pairs(a.q2 + base + po, 8 * grp, p < S, q2lo, q2hi);
-    prep_pairs2(q1lo, q1hi, q2lo, q2hi, 8 * grp, p, 0, 2, sp);
+    load_pairs(a.q1 + base + po, qd0, gap, p < S, q1lo, q1hi);
+    load_pairs(a.q2 + base + po, qd0, gap, p < S, q2lo, q2hi);
+    prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, sp);
     Q1[i][0] = to_f16x8(q1lo);
     Q1[i][1] = to_f16x8(q1hi);
     Q2[i][0] = to_f16x8(q2lo);
@@ -525,7 +604,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   const int T = t_hi - t_lo + 1;
   const int rbytes = S * HD * 2;
-  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(a.v + base, rbytes);
+  // with V flags the values come from the masked copy pass 1 wrote
+  const unsigned short* vsrc = a.v_keep ? reinterpret_cast<const unsigned short*>(a.ws) + 2 * nrows * HD : a.v;
+  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(vsrc + base, rbytes);
   uint4 r1[CPT], r2[CPT], rv[CPT];
   auto gload = [&](const rsrc_t& src, int u, uint4 (&r)[CPT]) {
 #pragma unroll
@@ -643,9 +724,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // ---------------------------------------------------------------- dispatch
 static bool use_band(int S, int window) { return window >= 0 && window < S - 1 && window <= BAND_MAX_WINDOW; }
 
-size_t diff_workspace_bytes(int B, int H, int S, int window) {
+// full path: k1^, k2^ (fp16) and, for calls with V flags, the flagged V (bf16)
+size_t diff_workspace_bytes(int B, int H, int S, int window, bool v_flags) {
   if (use_band(S, window)) return 0;
-  return (size_t)2 * B * H * S * HD * sizeof(_Float16);
+  return (size_t)(v_flags ? 3 : 2) * B * H * S * HD * sizeof(_Float16);
 }
 
 hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
@@ -658,22 +740,41 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
     int nblk = (int)(((long long)nb * BH + BAND_TARGET_WGS - 1) / BAND_TARGET_WGS);
     nblk = nblk < 1 ? 1 : (nblk > 16 ? 16 : nblk);
     dim3 grid((nb + nblk - 1) / nblk, BH);
-    if (a.window <= 24)
-      hipLaunchKernelGGL((diff_band<4, BAND_WPE>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
-    else
-      hipLaunchKernelGGL((diff_band<6, 2>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+    const bool narrow = a.window <= 24;
+    if (a.norm == NORM_RMS) {
+      if (narrow)
+        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+      else
+        hipLaunchKernelGGL((diff_band<6, 2, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+    } else {
+      if (narrow)
+        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+      else
+        hipLaunchKernelGGL((diff_band<6, 2, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+    }
     return hipGetLastError();
   }
   const size_t nrows = (size_t)BH * a.S;
-  hipLaunchKernelGGL(diff_kprep, dim3((unsigned)((nrows + 63) / 64)), dim3(256), 0, s, a);
+  const dim3 kgrid((unsigned)((nrows + 63) / 64));
+  if (a.norm == NORM_RMS)
+    hipLaunchKernelGGL(diff_kprep<NORM_RMS>, kgrid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(diff_kprep<NORM_DYT>, kgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int NQB = 1, NW = 4;
   dim3 grid((a.S + 16 * NQB * NW - 1) / (16 * NQB * NW), BH);
-  if (a.window >= 0)
-    hipLaunchKernelGGL((diff_flash<NQB, NW, true>), grid, dim3(64 * NW), 0, s, a);
-  else
-    hipLaunchKernelGGL((diff_flash<NQB, NW, false>), grid, dim3(64 * NW), 0, s, a);
+  if (a.norm == NORM_RMS) {
+    if (a.window >= 0)
+      hipLaunchKernelGGL((diff_flash<NQB, NW, true, NORM_RMS>), grid, dim3(64 * NW), 0, s, a);
+    else
+      hipLaunchKernelGGL((diff_flash<NQB, NW, false, NORM_RMS>), grid, dim3(64 * NW), 0, s, a);
+  } else {
+    if (a.window >= 0)
+      hipLaunchKernelGGL((diff_flash<NQB, NW, true, NORM_DYT>), grid, dim3(64 * NW), 0, s, a);
+    else
+      hipLaunchKernelGGL((diff_flash<NQB, NW, false, NORM_DYT>), grid, dim3(64 * NW), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -50,6 +50,13 @@ __device__ __forceinline__ float group4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the four consecutive lanes {4k .. 4k+3} (DPP quad permutations [1,0,3,2],
+// then [2,3,0,1]); every lane of the quad gets the same value.
+__device__ __forceinline__ float quad_sum(float x) {
+  const float y = x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  return y + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Lazily raised running maximum of the online softmax: the reference maximum moves
@@ -100,6 +107,9 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_FLAGS = 0x00020000;  // dword 3 of a raw (untyped) buffer descriptor
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, RSRC_FLAGS);
+}
+__device__ __forceinline__ unsigned buf_ld1(rsrc_t r, int byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, byte_offset, 0, 0);
 }
 __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, int byte_offset) {
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4;

@@ -22,15 +22,21 @@ struct DiffArgs {
   const unsigned short* k2;
   const unsigned short* v;
   unsigned short* o;
-  _Float16* ws;            // prepared keys (full path): [2][B][H][S][64] fp16
-  const float* alpha;      // [4]
-  const float* gamma;      // [4][64]
-  const float* beta;       // [4][64]
+  _Float16* ws;            // full path: k1^, k2^ [2][B][H][S][64] fp16, then (with v_keep) flagged V bf16
+  const float* alpha;      // [4]      DyT
+  const float* gamma;      // [4][64]  DyT
+  const float* beta;       // [4][64]  DyT
+  const float* rms_w;      // [4][64]  RMSNorm weight
   const float* lambda;     // [H]
+  const unsigned char* v_keep;  // [B][S] or null: a 0 flag zeroes that token's V row
+  int norm;                // 0: DyT, 1: RMSNorm
+  float rms_eps;
+  int rot32;               // 1: rotary on dims 0..31 (pairs i, i+16), dims 32..63 unrotated
   int B, H, S;
   int window;              // >= 0: |i - j| <= window; < 0: all keys
   float c;                 // scale * log2(e)
-  double rev[32];          // rope_base^(-2i/64) / (2 pi): revolutions per position of pair i
+  double rev[32];          // revolutions per position of pair i: rope_base^(-2i/64) / (2 pi), or with
+                           // rot32 rope_base^(-2i/32) / (2 pi) for i < 16 and 0 (no rotation) above
   float rev_hi[32];        // rev split for fp32 angle reduction: rev_hi * p exact for p < 2^split_bits
   float rev_lo[32];
   int split_angles;        // 1: S <= 2^16, use rev_hi/rev_lo; 0: fp64 angles
@@ -39,7 +45,7 @@ struct DiffArgs {
 // Largest window the one-pass band kernel takes; wider windows use the flash path.
 constexpr int BAND_MAX_WINDOW = 40;
 
-size_t diff_workspace_bytes(int B, int H, int S, int window);
+size_t diff_workspace_bytes(int B, int H, int S, int window, bool v_flags);
 hipError_t launch_diffattn(const DiffArgs& a, hipStream_t s);
 
 }  // namespace ka

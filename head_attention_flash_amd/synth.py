@@ -9,7 +9,11 @@ Recipe (the same for every workload): numpy Generator(PCG64(seed)); activations
 ~ N(0, 1) drawn in float64, narrowed to float32, then (for bf16) to bf16.  DyT
 gains gamma ~ U[2, 8] per tensor and channel, alpha = 0.5, beta = 0; lambda = 0.8
 per head; rope base 10000; scale 1/8.  Seeds are 1000*workload + tensor index
-(q/q1 = 0, k/k1 = 1, v = 2, q2 = 3, k2 = 4, gamma = 5).
+(q/q1 = 0, k/k1 = 1, v = 2, q2 = 3, k2 = 4, gamma = 5, RMSNorm weight = 6).
+
+Model forms of the differential workloads: RMSNorm weights ~ U[0.5, 1.5] per
+tensor and channel, eps 1e-6; V padding flags mark the last `pad` tokens of batch
+element b (pad + b of them) as padding, the layout of latents padded at the end.
 """
 from __future__ import annotations
 
@@ -113,3 +117,18 @@ def make_diff(wl: Workload, seed_base: int | None = None, S: int | None = None, 
     k2 = normal(base + 4, shape, "bf16")
     params = make_diff_params(H, base + 5)
     return (q1, k1, q2, k2, v), params
+
+
+def make_model_params(H: int, seed: int, lam: float = 0.8):
+    """RMSNorm weights [4, D] (set order q1, k1, q2, k2) and lambda [H], float32."""
+    return uniform(seed, (4, D), 0.5, 1.5), np.full(H, lam, dtype=np.float32)
+
+
+def make_v_keep(B: int, S: int, pad: int) -> np.ndarray:
+    """[B, S] uint8 flags: 1 = real token, 0 = padding (the last pad + b tokens of batch element b)."""
+    keep = np.ones((B, S), dtype=np.uint8)
+    for b in range(B):
+        n = min(S, pad + b)
+        if n > 0:
+            keep[b, S - n:] = 0
+    return keep

@@ -8,6 +8,8 @@
  *   ka_xattn_fwd     cross-attention against a short key set held on chip
  *   ka_diffattn_fwd  differential attention with DyT and rotary embedding on Q/K,
  *                    banded (+-window keys) or full
+ *   ka_diffattn_fwd_ex  the same with the Stable Audio 3 model's options: RMSNorm
+ *                    on Q/K, rotary on 32 of the 64 dims, a V padding mask
  *
  * Common conventions
  *   - Pointers q, k, v, q1, k1, q2, k2, o, the parameter arrays and the
@@ -104,8 +106,41 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
                           const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta, float rope_base,
                           const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes ka_diffattn_fwd needs for this shape (0 for the banded path).
- * Returns 0 for invalid shapes as well; ka_diffattn_fwd then reports the error. */
+/* Q/K normaliser of ka_diffattn_fwd_ex. */
+typedef enum { KA_QKNORM_DYT = 0, KA_QKNORM_RMS = 1 } ka_qknorm;
+
+/*
+ * Differential attention in the Stable Audio 3 model's own forms
+ * ("401 -> 163 ms: Stable Audio 3 medium on one TPU v6e chip", appendix D1, D3,
+ * D4, E1): ka_diffattn_fwd with three choices that call leaves fixed.
+ *   qk_norm       KA_QKNORM_DYT: DyT with dyt_alpha, dyt_gamma, dyt_beta, as in
+ *                 ka_diffattn_fwd (rms_weight is ignored and may be NULL).
+ *                 KA_QKNORM_RMS: per-head RMSNorm in fp32,
+ *                   x~[d] = rms_weight_t[d] * x[d] / sqrt(mean_d x[d]^2 + rms_eps),
+ *                 rms_weight [4][64] fp32 device (sets q1, k1, q2, k2), rms_eps > 0
+ *                 (the dyt_* pointers are ignored and may be NULL).
+ *   rotary_dims   64: rotate-half over all dims, as ka_diffattn_fwd.
+ *                 32: dims 0..31 only, dim i < 16 paired with dim i + 16 at
+ *                 theta_i = p * rope_base^(-2i/32); dims 32..63 pass through.
+ *   v_keep        NULL (every token kept), or [B][S] bytes on the device: a token
+ *                 whose byte is 0 contributes a zero V row; its key stays in both
+ *                 softmaxes (the model's padding mask, unlike key masking).
+ * Everything else -- shapes, dtype, window, lambda, workspace, errors -- is as for
+ * ka_diffattn_fwd; rotary_dims other than 32 or 64, or a non-positive or
+ * non-finite rms_eps, give KA_ERR_PARAM; an unknown qk_norm KA_ERR_UNSUPPORTED.
+ */
+ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                             const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                             ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
+                             const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
+                             float rope_base, const float* lambda, const uint8_t* v_keep, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes ka_diffattn_fwd and ka_diffattn_fwd_ex need for this shape: 0 for
+ * the banded path; for the full path the prepared keys (2*B*H*S*64 fp16) plus room
+ * for a flagged copy of V (B*H*S*64 bf16), which only calls with v_keep use (without
+ * v_keep the first 2*B*H*S*64*2 bytes suffice).  Returns 0 for invalid shapes as
+ * well; the call then reports the error. */
 size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window);
 
 /* Static description of a status code. */

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_header_declares_the_three_operations():
     syms = declared_symbols()
-    for s in ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd"):
+    for s in ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_fwd_ex"):
         assert s in syms
 
 
@@ -100,9 +100,9 @@ def test_diff_validation(lib):
     assert diff(lib, scale=-1.0) == _lib.KA_ERR_PARAM
     assert diff(lib, v=A + 4) == _lib.KA_ERR_ALIGN
     assert diff(lib, o=Q + 64) == _lib.KA_ERR_ALIAS
-    # the full path needs a workspace
-    need = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
-    assert need == 2 * 1 * 2 * 8 * 64 * 2
+    # the full path needs a workspace: the prepared keys (the reported size also covers a flagged V)
+    assert lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1) == 3 * 1 * 2 * 8 * 64 * 2
+    need = 2 * 1 * 2 * 8 * 64 * 2
     assert diff(lib, window=-1) == _lib.KA_ERR_NULL
     assert diff(lib, window=-1, ws=W, ws_bytes=need - 1) == _lib.KA_ERR_WORKSPACE
     assert diff(lib, window=-1, ws=W + 8, ws_bytes=need) == _lib.KA_ERR_ALIGN
@@ -111,14 +111,47 @@ def test_diff_validation(lib):
     assert lib.ka_last_hip_error() == 0
 
 
+KEEP = 0x100000 * 12
+
+
+def diff_ex(lib, dt=ka.KA_BF16, q1=Q, k1=K, q2=V, k2=O2, v=A, o=O, B=1, H=2, Sq=8, Sk=8, D=64, scale=0.125,
+            window=2, norm=ka.KA_QKNORM_RMS, alpha=0, gamma=0, beta=0, rms_w=G, eps=1e-6, rot=32, base=10000.0,
+            lam=L, keep=KEEP, ws=0, ws_bytes=0):
+    return lib.ka_diffattn_fwd_ex(dt, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, ctypes.c_float(scale), window, norm,
+                                  alpha, gamma, beta, rms_w, ctypes.c_float(eps), rot, ctypes.c_float(base), lam,
+                                  keep, ws, ws_bytes, None)
+
+
+def test_diff_ex_validation(lib):
+    # every case fails before any HIP call
+    assert diff_ex(lib, norm=7) == _lib.KA_ERR_UNSUPPORTED
+    assert diff_ex(lib, rms_w=0) == _lib.KA_ERR_NULL
+    assert diff_ex(lib, norm=ka.KA_QKNORM_DYT) == _lib.KA_ERR_NULL  # DyT parameters missing
+    assert diff_ex(lib, norm=ka.KA_QKNORM_DYT, alpha=A + 0x80000, gamma=G, beta=BT, o=Q) == _lib.KA_ERR_ALIAS
+    for name in ("q1", "k1", "q2", "k2", "v", "o", "lam"):
+        assert diff_ex(lib, **{name: 0}) == _lib.KA_ERR_NULL, name
+    assert diff_ex(lib, rot=48) == _lib.KA_ERR_PARAM
+    assert diff_ex(lib, rot=0) == _lib.KA_ERR_PARAM
+    assert diff_ex(lib, eps=0.0) == _lib.KA_ERR_PARAM
+    assert diff_ex(lib, eps=float("nan")) == _lib.KA_ERR_PARAM
+    assert diff_ex(lib, Sk=9) == _lib.KA_ERR_SHAPE
+    assert diff_ex(lib, D=128) == _lib.KA_ERR_UNSUPPORTED
+    assert diff_ex(lib, o=KEEP) == _lib.KA_ERR_ALIAS  # o over the V flags
+    # with V flags the full path needs the larger workspace
+    need3 = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
+    assert diff_ex(lib, window=-1, ws=W, ws_bytes=need3 - 1) == _lib.KA_ERR_WORKSPACE
+    assert diff_ex(lib, window=-1, ws=KEEP - need3 + 16, ws_bytes=need3) == _lib.KA_ERR_ALIAS
+    assert lib.ka_last_hip_error() == 0
+
+
 def test_workspace_sizes(lib):
     # banded windows the one-pass kernel takes need no workspace
     assert lib.ka_diffattn_workspace_bytes(1, 8, 23086, 64, 17) == 0
     assert lib.ka_diffattn_workspace_bytes(1, 8, 23086, 64, 40) == 0
     # wide windows and the full window prepare keys once into the workspace
-    assert lib.ka_diffattn_workspace_bytes(1, 16, 1422, 64, -1) == 2 * 16 * 1422 * 64 * 2
-    assert lib.ka_diffattn_workspace_bytes(1, 8, 100, 64, 41) == 2 * 8 * 100 * 64 * 2
-    assert lib.ka_diffattn_workspace_bytes(1, 8, 30, 64, 29) == 2 * 8 * 30 * 64 * 2  # window >= S-1: full
+    assert lib.ka_diffattn_workspace_bytes(1, 16, 1422, 64, -1) == 3 * 16 * 1422 * 64 * 2
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 100, 64, 41) == 3 * 8 * 100 * 64 * 2
+    assert lib.ka_diffattn_workspace_bytes(1, 8, 30, 64, 29) == 3 * 8 * 30 * 64 * 2  # window >= S-1: full
     assert lib.ka_diffattn_workspace_bytes(0, 8, 100, 64, -1) == 0
     assert lib.ka_diffattn_workspace_bytes(1, 8, 100, 32, -1) == 0
 

@@ -291,3 +291,93 @@ def test_graph_capture_replays_match_eager():
         del junk
         for a, b in zip(outs, eager):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep} differs"
+
+
+# ------------------------------------------------------------------ differential, model forms
+
+def _run_diff_ex(inputs, params, window, norm, rot, keep, scale=0.125, base=10000.0, eps=1e-6):
+    q1, k1, q2, k2, v = (to_dev(x) for x in inputs)
+    o = nan_like(q1)
+    kw = dict(o=o, scale=scale, window=window, qk_norm=norm, rotary_dims=rot, rope_base=base)
+    if norm == "rms":
+        w, lm = params
+        kw.update(rms_weight=to_dev(w), rms_eps=eps)
+    else:
+        a, g, b, lm = params
+        kw.update(alpha=to_dev(a), gamma=to_dev(g), beta=to_dev(b))
+    if keep is not None:
+        kw["v_keep"] = to_dev(keep)
+    ka.ka_diffattn_fwd_ex(q1, k1, q2, k2, v, to_dev(lm), **kw)
+    torch.cuda.synchronize()
+    return to_host_f64(o)
+
+
+def _oracle_diff_ex(inputs, params, window, norm, rot, keep, rows=None, scale=0.125, base=10000.0, eps=1e-6):
+    if norm == "rms":
+        w, lm = params
+        return oracle.diffattn(*inputs, scale, window, None, None, None, base, lm, rows=rows, norm="rms",
+                               rms_weight=w, rms_eps=eps, rotary_dims=rot, v_keep=keep)
+    a, g, b, lm = params
+    return oracle.diffattn(*inputs, scale, window, a, g, b, base, lm, rows=rows, rotary_dims=rot, v_keep=keep)
+
+
+def _model_case(norm, S, H, B, seed):
+    wl = W["sa3_dit_fulldiff_h16s1422"]
+    inputs, params = synth.make_diff(wl, seed_base=seed, S=S, H=H, B=B)
+    if norm == "rms":
+        params = synth.make_model_params(H, seed + 6)
+    return inputs, params
+
+
+@pytest.mark.parametrize("norm", ["dyt", "rms"])
+@pytest.mark.parametrize("rot", [64, 32])
+@pytest.mark.parametrize("padded", [False, True])
+@pytest.mark.parametrize("window", [17, 100, -1])
+def test_diff_model_forms(norm, rot, padded, window):
+    """Every combination of normaliser, rotary width and V flags on the banded, wide-window and full paths."""
+    S, H, B = 300, 2, 2
+    inputs, params = _model_case(norm, S, H, B, 1200 + 10 * rot + (5 if padded else 0) + max(window, 0))
+    keep = synth.make_v_keep(B, S, 37) if padded else None
+    got = _run_diff_ex(inputs, params, window, norm, rot, keep)
+    want = _oracle_diff_ex(inputs, params, window, norm, rot, keep)
+    assert_close(got, want, BF16_TOL, f"model form norm={norm} rot={rot} padded={padded} w={window}")
+
+
+@pytest.mark.parametrize("norm", ["dyt", "rms"])
+def test_diff_model_band_strips(norm):
+    """RMSNorm's row reductions in the key ring fill and the per-block staging, many strips."""
+    S, H, B = 700, 48, 2
+    inputs, params = _model_case(norm, S, H, B, 1300)
+    keep = synth.make_v_keep(B, S, 60)
+    got = _run_diff_ex(inputs, params, 17, norm, 32, keep)
+    assert_close(got, _oracle_diff_ex(inputs, params, 17, norm, 32, keep), BF16_TOL, f"model strips {norm}")
+
+
+def test_diff_model_all_padded_is_zero():
+    inputs, params = _model_case("rms", 200, 2, 1, 1400)
+    keep = np.zeros((1, 200), dtype=np.uint8)
+    for window in (17, -1):
+        assert np.all(_run_diff_ex(inputs, params, window, "rms", 32, keep) == 0.0)
+
+
+def test_diff_model_dit_workload_sampled():
+    """The DiT's own form at the full-differential workload's size: RMSNorm, 32 rotary dims, the last
+    142 tokens padded."""
+    wl = W["sa3_dit_fulldiff_h16s1422"]
+    inputs, _ = synth.make_diff(wl)
+    params = synth.make_model_params(wl.H, 1000 * wl.index + 6)
+    keep = synth.make_v_keep(wl.B, wl.Sq, 142)
+    got = _run_diff_ex(inputs, params, wl.window, "rms", 32, keep, wl.scale).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 3000, 19, edge=3, period=64)
+    want = _oracle_diff_ex(inputs, params, wl.window, "rms", 32, keep, rows=rows, scale=wl.scale)
+    assert_close(got[rows], want, BF16_TOL, "dit model form")
+
+
+def test_diff_model_decoder_workload_sampled():
+    """The decoder's own form at the banded workload's size: DyT, 32 rotary dims."""
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl)
+    got = _run_diff_ex(inputs, params, wl.window, "dyt", 32, None, wl.scale).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 1500, 23, edge=40, period=128)
+    want = _oracle_diff_ex(inputs, params, wl.window, "dyt", 32, None, rows=rows, scale=wl.scale)
+    assert_close(got[rows], want, BF16_TOL, "decoder model form")
