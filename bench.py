@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--forms", default="cross,band,full,band_model,full_model",
+    ap.add_argument("--forms", default="cross,cross_l1,cross_cond257,band,full,band_model,full_model",
                     help="extra forms to time (comma list, or 'none')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
@@ -223,6 +223,26 @@ def main():
                           "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
                           "bound": "hbm", "flops": f, "bytes": b, "input_copies": len(sets)}
         log(f"bench: cross {forms['cross']}")
+        del sets, outs
+    # ---------------- more conditioning shapes: SDXL level-1 cross (77 keys), the DiT's 257 tokens (streamed)
+    for name, key, kern in (("cross_l1", "sdxl_l1_cross_b2h10q4096k77", "xattn_bf16"),
+                            ("cross_cond257", "sa3_dit_cross_h24q1422k257", "attn_bf16 (keys streamed)")):
+        if name not in wanted:
+            continue
+        wl = synth.WORKLOADS[key]
+        log(f"bench: {wl.desc}")
+        f, b = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk), acc.dense_bytes(wl.B, wl.H, wl.Sq, wl.Sk)
+        n = max(2, min(64, -(-600_000_000 // b)))  # input copies: 600 MB, past the 256 MB last-level cache
+        sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s)] for s in range(n)]
+        outs = [torch.empty_like(s[0]) for s in sets]
+        sec = time_graph(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
+                         args.warmup, torch)
+        forms[name] = {"workload": wl.key, "kernel": kern, "us": round(sec * 1e6, 3),
+                       "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
+                       "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
+                       "bound": "hbm" if f / b < acc.MFMA_BF16_PEAK / acc.HBM_PEAK else "mfma", "flops": f, "bytes": b,
+                       "input_copies": len(sets)}
+        log(f"bench: {name} {forms[name]}")
         del sets, outs
     # ---------------- banded differential attention (HBM-bound: 3 copies = 425 MB > 256 MB cache)
     if "band" in wanted:

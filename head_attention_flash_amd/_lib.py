@@ -117,7 +117,7 @@ def ka_attn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
 
 
 def ka_xattn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
-    """Cross-attention against a short key set (Sk <= 256) held on chip. Returns o."""
+    """Cross-attention: key sets up to 256 held on chip, longer ones streamed. Returns o."""
     lib = load()
     B, H, Sq, D = q.shape
     Sk = k.shape[2]

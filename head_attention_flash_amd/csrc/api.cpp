@@ -78,7 +78,10 @@ ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void*
   size_t qb = 0, kb = 0;
   ka_status st = check_dense(dtype, q, k, v, o, B, H, Sq, Sk, D, scale, &qb, &kb);
   if (st != KA_OK) return st;
-  if (Sk > KA_XATTN_MAX_SK) return KA_ERR_SHAPE;
+  if (dtype == KA_BF16 && Sk > KA_XATTN_MAX_SK)  // too many keys to hold on chip: stream them in tiles
+    return hip_status(ka::launch_attn_bf16(static_cast<const unsigned short*>(q), static_cast<const unsigned short*>(k),
+                                           static_cast<const unsigned short*>(v), static_cast<unsigned short*>(o), B,
+                                           H, Sq, Sk, scale, stream));
   if (dtype == KA_F32)
     return hip_status(ka::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                           static_cast<const float*>(v), static_cast<float*>(o), B, H, Sq, Sk, scale,

@@ -68,6 +68,11 @@ WORKLOADS = {
                                         desc="SDXL level-1 self-attention (64x64 latent), bf16, B=2 H=10 S=4096"),
     "sdxl_l2_cross_b2h20q1024k77": Workload("sdxl_l2_cross_b2h20q1024k77", "cross", "bf16", 2, 20, 1024, 77, index=3,
                                             desc="SDXL level-2 cross-attention, bf16, B=2 H=20 Sq=1024 Sk=77"),
+    "sdxl_l1_cross_b2h10q4096k77": Workload("sdxl_l1_cross_b2h10q4096k77", "cross", "bf16", 2, 10, 4096, 77, index=6,
+                                            desc="SDXL level-1 cross-attention, bf16, B=2 H=10 Sq=4096 Sk=77"),
+    "sa3_dit_cross_h24q1422k257": Workload("sa3_dit_cross_h24q1422k257", "cross", "bf16", 1, 24, 1422, 257, index=7,
+                                           desc="cross-attention to 257 conditioning tokens, DiT-shaped, bf16, "
+                                                "B=1 H=24 Sq=1422 Sk=257"),
     "sa3_decoder_banddiff_h8s23086w17": Workload("sa3_decoder_banddiff_h8s23086w17", "diff", "bf16", 1, 8, 23086,
                                                  23086, window=17, index=4,
                                                  desc="banded differential attention, decoder-shaped, bf16, "

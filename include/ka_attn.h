@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { KA_F32 = 0, KA_BF16 = 1 } ka_dtype;
 
-/* Largest key count ka_xattn_fwd holds on chip. */
+/* Largest key count ka_xattn_fwd holds on chip (longer key sets stream through). */
 #define KA_XATTN_MAX_SK 256
 
 /*
@@ -73,10 +73,13 @@ ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* 
                       int Sk, int D, float scale, hipStream_t stream);
 
 /*
- * Cross-attention: the same definition as ka_attn_fwd, for a short key set
- * (1 <= Sk <= KA_XATTN_MAX_SK, e.g. SDXL's 77 text-context tokens, "SDXL as a
- * requirements inventory" s1.2 and s5.7).  All Sk keys and values of a (b, h)
- * are held in LDS and re-read by every query tile; queries stream through.
+ * Cross-attention: the same definition as ka_attn_fwd, for a key set of
+ * conditioning tokens (SDXL's 77 text-context tokens, "SDXL as a requirements
+ * inventory" s1.2 and s5.7; Stable Audio 3's 257 conditioning tokens, "401 ->
+ * 163 ms..." appendix D2).  With 1 <= Sk <= KA_XATTN_MAX_SK all keys and values
+ * of a (b, h) are held in LDS and re-read by every query tile, queries streaming
+ * through; longer key sets stream through LDS in tiles (the ka_attn_fwd kernels).
+ * Any Sk >= 1.
  *   dtype KA_BF16 (KA_F32 is accepted and routed to the fp32 kernel).
  */
 ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,

@@ -78,8 +78,10 @@ def test_dense_validation(lib, fn):
     assert lib.ka_last_hip_error() == 0
 
 
-def test_xattn_key_limit(lib):
-    assert dense(lib, "ka_xattn_fwd", Sk=ka.KA_XATTN_MAX_SK + 1) == _lib.KA_ERR_SHAPE
+def test_xattn_takes_long_key_sets(lib):
+    # past the on-chip limit the keys stream: the only shape limits left are the dense ones
+    assert dense(lib, "ka_xattn_fwd", Sk=ka.KA_XATTN_MAX_SK + 1, o=Q) == _lib.KA_ERR_ALIAS
+    assert dense(lib, "ka_xattn_fwd", Sk=(1 << 31) - 1) == _lib.KA_ERR_SHAPE  # 32-bit buffer offsets
 
 
 def diff(lib, dt=ka.KA_BF16, q1=Q, k1=K, q2=V, k2=O2, v=A, o=O, B=1, H=2, Sq=8, Sk=8, D=64, scale=0.125, window=2,

@@ -381,3 +381,23 @@ def test_diff_model_decoder_workload_sampled():
     rows = _rows_sample(wl.B, wl.H, wl.Sq, 1500, 23, edge=40, period=128)
     want = _oracle_diff_ex(inputs, params, wl.window, "dyt", 32, None, rows=rows, scale=wl.scale)
     assert_close(got[rows], want, BF16_TOL, "decoder model form")
+
+
+# ------------------------------------------------------------------ cross-attention shapes
+
+@pytest.mark.parametrize("key", ["sdxl_l1_cross_b2h10q4096k77", "sa3_dit_cross_h24q1422k257"])
+def test_xattn_conditioning_workloads(key):
+    """SDXL level-1 cross-attention (77 keys, on chip) and the DiT's 257 conditioning tokens
+    (streamed), every output row against the oracle."""
+    wl = W[key]
+    q, k, v = synth.make_dense(wl)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v, wl.scale)
+    assert_close(got, oracle.attn(q, k, v, wl.scale), BF16_TOL, wl.key)
+
+
+@pytest.mark.parametrize("Sk", [255, 256, 257, 300, 511, 1000])
+def test_xattn_around_the_on_chip_limit(Sk):
+    wl = W["sdxl_l2_cross_b2h20q1024k77"]
+    q, k, v = synth.make_dense(wl, seed_base=1500 + Sk, B=1, H=3, Sq=333, Sk=Sk)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"xattn Sk={Sk}")
