@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--forms", default="cross,cross_l1,cross_cond257,band,full,band_model,full_model",
+    ap.add_argument("--forms", default="cross,cross_l1,cross_cond257,band,full,band_model,full_model,band_fused",
                     help="extra forms to time (comma list, or 'none')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
@@ -307,6 +307,35 @@ def main():
                                     "input_copies": len(sets)}
         log(f"bench: band model form {forms['band_diff_model']}")
         del sets, outs
+    if "band_fused" in wanted:
+        # the decoder form reading q1, k1, v, q2, k2 straight out of one [B, S, 5, H, 64] projection and
+        # writing the merged [B, S, H, 64] output (strided views, no transposes)
+        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
+        log(f"bench: {wl.desc}, decoder form on a fused projection")
+        sets = []
+        for s_ in range(3):
+            ins, prm = synth.make_diff(wl, seed_base=1000 * wl.index + 10 * s_)
+            t = [up(x, torch) for x in ins]  # q1, k1, q2, k2, v
+            X = torch.stack([x.permute(0, 2, 1, 3) for x in (t[0], t[1], t[4], t[2], t[3])], dim=2).contiguous()
+            del t
+            views = [X[:, :, i].permute(0, 2, 1, 3) for i in (0, 1, 3, 4, 2)]
+            out = torch.empty(wl.B, wl.Sq, wl.H, 64, dtype=torch.bfloat16, device="cuda")
+            sets.append((X, views, out, [up(x, torch) for x in prm]))
+        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
+
+        def band_fused(i):
+            _, views, out, (a_, g_, b_, l_) = sets[i]
+            ka.ka_diffattn_fwd_ex(*views, l_, o=out.permute(0, 2, 1, 3), scale=wl.scale, window=wl.window,
+                                  qk_norm="dyt", alpha=a_, gamma=g_, beta=b_, rotary_dims=32)
+
+        sec = time_graph(band_fused, len(sets), args.steps, args.warmup, torch)
+        forms["band_diff_fused"] = {"workload": wl.key, "options": "DyT, rotary on 32 of 64 dims, inputs read from "
+                                    "a fused [B,S,5,H,64] projection, output written [B,S,H,64]",
+                                    "kernel": "diff_band", "us": round(sec * 1e6, 3), "GB/s": round(b / sec / 1e9, 1),
+                                    "hbm_frac": round(b / sec / acc.HBM_PEAK, 4), "bound": "hbm", "bytes": b,
+                                    "input_copies": len(sets)}
+        log(f"bench: band fused {forms['band_diff_fused']}")
+        del sets
     if "full_model" in wanted:
         wl = synth.WORKLOADS["sa3_dit_fulldiff_h16s1422"]
         pad = 142

@@ -53,7 +53,7 @@ def load(path: str = LIB_PATH):
     lib.ka_diffattn_fwd.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, f, vp, vp, sz, vp]
     lib.ka_diffattn_fwd.restype = i
     lib.ka_diffattn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, vp, vp, f, i, f, vp,
-                                       vp, vp, sz, vp]
+                                       vp, vp, vp, sz, vp]
     lib.ka_diffattn_fwd_ex.restype = i
     lib.ka_diffattn_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.ka_diffattn_workspace_bytes.restype = sz
@@ -89,6 +89,20 @@ def _dev(t, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, S, D]")
     return ctypes.c_void_p(t.data_ptr())
+
+
+class KaLayout(ctypes.Structure):
+    """ka_layout: element strides (batch, head, token) of a [B][H][S][64] view."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+def _dev_view(t, name: str):
+    """A [B, H, S, 64] GPU view whose last dim is contiguous; returns (pointer, ka_layout)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a [B, H, S, D] view with contiguous D")
+    return ctypes.c_void_p(t.data_ptr()), KaLayout(t.stride(0), t.stride(1), t.stride(2))
 
 
 def _stream(stream):
@@ -163,6 +177,8 @@ def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, win
     """Differential attention (bf16) in the model forms: qk_norm "dyt" (alpha [4], gamma/beta [4,64]) or
     "rms" (rms_weight [4,64], rms_eps); rotary_dims 64 or 32; v_keep: optional [B,S] uint8 GPU tensor
     (0 = that token's V row is zero, its key stays).  All parameter tensors are fp32 GPU tensors.
+    q1, k1, q2, k2, v and o may be strided [B, H, S, 64] views (e.g. slices of a fused projection);
+    their strides are passed as ka_layout views.
     """
     lib = load()
     B, H, S, D = q1.shape
@@ -177,10 +193,15 @@ def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, win
     opt = lambda t, name: _dev(t, name) if t is not None else ctypes.c_void_p(0)  # noqa: E731
     if v_keep is not None and v_keep.dtype != _torch().uint8:
         raise TypeError("v_keep must be a uint8 tensor")
-    st = lib.ka_diffattn_fwd_ex(_dtype_code(q1), _dev(q1, "q1"), _dev(k1, "k1"), _dev(q2, "q2"), _dev(k2, "k2"),
-                                _dev(v, "v"), _dev(o, "o"), B, H, S, S, D, float(scale), int(window), norm,
-                                opt(alpha, "alpha"), opt(gamma, "gamma"), opt(beta, "beta"),
+    views = [_dev_view(t, n) for t, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (o, "o"))]
+    layouts = None
+    if not all(t.is_contiguous() for t in (q1, k1, q2, k2, v, o)):
+        layouts = (KaLayout * 6)(*[lay for _, lay in views])
+    st = lib.ka_diffattn_fwd_ex(_dtype_code(q1), *[ptr for ptr, _ in views], B, H, S, S, D, float(scale), int(window),
+                                norm, opt(alpha, "alpha"), opt(gamma, "gamma"), opt(beta, "beta"),
                                 opt(rms_weight, "rms_weight"), float(rms_eps), int(rotary_dims), float(rope_base),
-                                _dev(lam, "lambda"), opt(v_keep, "v_keep"), ws_ptr, ws_bytes, _stream(stream))
+                                _dev(lam, "lambda"), opt(v_keep, "v_keep"),
+                                ctypes.cast(layouts, ctypes.c_void_p) if layouts is not None else None, ws_ptr,
+                                ws_bytes, _stream(stream))
     _check(lib, st, "ka_diffattn_fwd_ex")
     return o

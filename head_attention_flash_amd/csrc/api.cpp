@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <utility>
 
 #include "ka_attn.h"
 #include "ka_kernels.hpp"
@@ -55,6 +56,39 @@ ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, 
   return KA_OK;
 }
 
+// A [B][H][S][64] bf16 view with element strides (batch, head, token): checks that every
+// stride is a non-negative multiple of 8 (16-byte rows), the token stride at least 64, one
+// (b, h) slice within the kernels' 32-bit buffer offsets, and the whole extent within 2^62
+// bytes.  *extent = bytes from the base to the end of the last row.
+bool view_ok(const ka_layout& L, int B, int H, int S, size_t* extent) {
+  if (L.batch < 0 || L.head < 0 || L.token < 64) return false;
+  if ((L.batch | L.head | L.token) & 7) return false;
+  const unsigned __int128 slice = ((unsigned __int128)(S - 1) * (unsigned long long)L.token + 64) * 2;
+  if (slice > 0x7fffffffu) return false;
+  const unsigned __int128 last = (unsigned __int128)(B - 1) * (unsigned long long)L.batch +
+                                 (unsigned __int128)(H - 1) * (unsigned long long)L.head +
+                                 (unsigned __int128)(S - 1) * (unsigned long long)L.token + 64;
+  if ((last * 2) >> 62) return false;
+  *extent = (size_t)(last * 2);
+  return true;
+}
+
+// No two (b, h, s) rows of the view share an element: sorted by stride (dims of extent 1
+// left out), each stride covers everything the smaller ones span.
+bool view_injective(const ka_layout& L, int B, int H, int S) {
+  struct D { long long stride, n; } d[3] = {{L.batch, B}, {L.head, H}, {L.token, S}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (d[j].stride < d[i].stride) std::swap(d[i], d[j]);
+  long long span = 64;  // one row
+  for (const D& x : d) {
+    if (x.n == 1) continue;
+    if (x.stride < span) return false;
+    span = x.stride * (x.n - 1) + span;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,8 +135,8 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
                              const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
                              ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
                              const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
-                             float rope_base, const float* lambda, const uint8_t* v_keep, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             float rope_base, const float* lambda, const uint8_t* v_keep, const ka_layout* layouts,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (qk_norm != KA_QKNORM_DYT && qk_norm != KA_QKNORM_RMS) return KA_ERR_UNSUPPORTED;
   if (!q1 || !k1 || !q2 || !k2 || !v || !o || !lambda) return KA_ERR_NULL;
   if (qk_norm == KA_QKNORM_DYT && (!dyt_alpha || !dyt_gamma || !dyt_beta)) return KA_ERR_NULL;
@@ -117,6 +151,14 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
   size_t tb = 0;
   if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
   if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  // views of q1, k1, q2, k2, v, o: the given strides, or contiguous [B][H][S][64]
+  ka_layout lay[6];
+  size_t ext[6];
+  for (int t = 0; t < 6; ++t) {
+    lay[t] = layouts ? layouts[t] : ka_layout{(int64_t)H * S * 64, (int64_t)S * 64, 64};
+    if (!view_ok(lay[t], B, H, S, &ext[t])) return KA_ERR_SHAPE;
+  }
+  if (!view_injective(lay[5], B, H, S)) return KA_ERR_SHAPE;  // rows of o written twice
   const void* ins[5] = {q1, k1, q2, k2, v};
   for (const void* p : ins)
     if (!aligned16(p)) return KA_ERR_ALIGN;
@@ -127,15 +169,16 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
     if (workspace_bytes < need) return KA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KA_ERR_ALIGN;
   }
-  for (const void* p : ins)
-    if (overlap(o, tb, p, tb)) return KA_ERR_ALIAS;
-  if (need && overlap(o, tb, workspace, need)) return KA_ERR_ALIAS;
+  // the extents [base, base + ext) of the views; inputs may share memory with each other
+  for (int t = 0; t < 5; ++t)
+    if (overlap(o, ext[5], ins[t], ext[t])) return KA_ERR_ALIAS;
+  if (need && overlap(o, ext[5], workspace, need)) return KA_ERR_ALIAS;
   if (need)
-    for (const void* p : ins)
-      if (overlap(workspace, need, p, tb)) return KA_ERR_ALIAS;
+    for (int t = 0; t < 5; ++t)
+      if (overlap(workspace, need, ins[t], ext[t])) return KA_ERR_ALIAS;
   if (v_keep) {
     const size_t nk = (size_t)B * S;
-    if (overlap(o, tb, v_keep, nk) || (need && overlap(workspace, need, v_keep, nk))) return KA_ERR_ALIAS;
+    if (overlap(o, ext[5], v_keep, nk) || (need && overlap(workspace, need, v_keep, nk))) return KA_ERR_ALIAS;
   }
 
   ka::DiffArgs a;
@@ -159,6 +202,11 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
   a.B = B;
   a.H = H;
   a.S = S;
+  for (int t = 0; t < 6; ++t) {
+    a.sb[t] = lay[t].batch;
+    a.sh[t] = lay[t].head;
+    a.st[t] = (int)lay[t].token;
+  }
   a.window = window < 0 ? -1 : window;
   a.c = scale * 1.4426950408889634f;
   const double two_pi = 6.283185307179586476925286766559;
@@ -190,7 +238,7 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
                           const float* lambda, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dyt_alpha || !dyt_gamma || !dyt_beta) return KA_ERR_NULL;
   return ka_diffattn_fwd_ex(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, KA_QKNORM_DYT, dyt_alpha,
-                            dyt_gamma, dyt_beta, nullptr, 1.0f, 64, rope_base, lambda, nullptr, workspace,
+                            dyt_gamma, dyt_beta, nullptr, 1.0f, 64, rope_base, lambda, nullptr, nullptr, workspace,
                             workspace_bytes, stream);
 }
 

@@ -93,6 +93,15 @@ __device__ __forceinline__ void load_params(SharedParams& sp, const DiffArgs& a)
 __device__ __forceinline__ int lo_dim(int c, bool rot32) { return rot32 && c >= 2 ? 8 * c + 16 : 8 * c; }
 __device__ __forceinline__ int pair_gap(bool rot32) { return rot32 ? 16 : 32; }
 
+// Tensor t (0..5: q1, k1, q2, k2, v, o) of batch element b, head h: the first element of its
+// [S][64] slice; token j then sits j * st[t] elements further.
+enum { TQ1 = 0, TK1 = 1, TQ2 = 2, TK2 = 3, TV = 4, TO = 5 };
+__device__ __forceinline__ size_t slice_at(const DiffArgs& a, int t, size_t b, size_t h) {
+  return b * (size_t)a.sb[t] + h * (size_t)a.sh[t];
+}
+// bytes a buffer resource over one slice spans: S rows at stride st[t], the last one 128 bytes
+__device__ __forceinline__ int slice_bytes(const DiffArgs& a, int t) { return ((a.S - 1) * a.st[t] + HD) * 2; }
+
 // Lanes holding one head row: four consecutive lanes (RED_QUAD) or {l, l^16, l^32,
 // l^48} (RED_GROUP4).
 constexpr int RED_QUAD = 0, RED_GROUP4 = 1;
@@ -194,16 +203,17 @@ struct RowStage {
 // index ([S] bytes), read only when the call passes them.
 struct BandSrc {
   rsrc_t k1, k2, v, keep;
+  int rk1, rk2, rv;  // token strides in bytes
   bool has_keep;
 };
 __device__ __forceinline__ void stage_load(RowStage& st, const BandSrc& src, int j, int cc, int d0, int gap) {
-  const int off = j * (HD * 2);
-  st.k1lo = buf_ld16(src.k1, off + 2 * d0);
-  st.k1hi = buf_ld16(src.k1, off + 2 * (d0 + gap));
-  st.k2lo = buf_ld16(src.k2, off + 2 * d0);
-  st.k2hi = buf_ld16(src.k2, off + 2 * (d0 + gap));
-  st.v0 = buf_ld16(src.v, off + 32 * cc);
-  st.v1 = buf_ld16(src.v, off + 32 * cc + 16);
+  const int o1 = j * src.rk1, o2 = j * src.rk2, ov = j * src.rv;
+  st.k1lo = buf_ld16(src.k1, o1 + 2 * d0);
+  st.k1hi = buf_ld16(src.k1, o1 + 2 * (d0 + gap));
+  st.k2lo = buf_ld16(src.k2, o2 + 2 * d0);
+  st.k2hi = buf_ld16(src.k2, o2 + 2 * (d0 + gap));
+  st.v0 = buf_ld16(src.v, ov + 32 * cc);
+  st.v1 = buf_ld16(src.v, ov + 32 * cc + 16);
   // past either end the flag reads 0, and the V row there is zero anyway
   st.vkeep = src.has_keep ? buf_ld1(src.keep, j) : 1u;
 }
@@ -311,15 +321,20 @@ void diff_band(DiffArgs a, int nblk) {
   const int S = a.S, window = a.window;
   const size_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const size_t base = bh * (size_t)S * HD;
+  const size_t bb = bh / a.H;
   const int strip0 = blockIdx.x * nblk * BAND_BM;
   const int pos0 = strip0 - HALO;  // position held by ring slot 0
   // one (b, h) slice of each tensor; rows outside [0, S) read as zero
-  const int rbytes = S * HD * 2;
   const bool has_keep = a.v_keep != nullptr;
-  const BandSrc src{make_rsrc(a.k1 + base, rbytes), make_rsrc(a.k2 + base, rbytes), make_rsrc(a.v + base, rbytes),
-                    make_rsrc(has_keep ? static_cast<const void*>(a.v_keep + (bh / a.H) * (size_t)S) : a.v, S), has_keep};
-  const rsrc_t q1rs = make_rsrc(a.q1 + base, rbytes), q2rs = make_rsrc(a.q2 + base, rbytes);
+  const BandSrc src{make_rsrc(a.k1 + slice_at(a, TK1, bb, h), slice_bytes(a, TK1)),
+                    make_rsrc(a.k2 + slice_at(a, TK2, bb, h), slice_bytes(a, TK2)),
+                    make_rsrc(a.v + slice_at(a, TV, bb, h), slice_bytes(a, TV)),
+                    make_rsrc(has_keep ? static_cast<const void*>(a.v_keep + bb * (size_t)S) : a.v, S),
+                    2 * a.st[TK1], 2 * a.st[TK2], 2 * a.st[TV], has_keep};
+  const rsrc_t q1rs = make_rsrc(a.q1 + slice_at(a, TQ1, bb, h), slice_bytes(a, TQ1));
+  const rsrc_t q2rs = make_rsrc(a.q2 + slice_at(a, TQ2, bb, h), slice_bytes(a, TQ2));
+  const int rq1 = 2 * a.st[TQ1], rq2 = 2 * a.st[TQ2];
+  unsigned short* const oslice = a.o + slice_at(a, TO, bb, h);
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), kd0 = lo_dim(cc, rot32), qd0 = lo_dim(grp, rot32);
   load_params<NORM>(sp, a);
@@ -351,11 +366,11 @@ void diff_band(DiffArgs a, int nblk) {
   // queries of this wave for block 0
   uint4 qs[4];
   auto qload = [&](int r0) {
-    const int off = (r0 + 16 * w + col) * (HD * 2) + 2 * qd0;  // rows past S read as zero
-    qs[0] = buf_ld16(q1rs, off);
-    qs[1] = buf_ld16(q1rs, off + 2 * gap);
-    qs[2] = buf_ld16(q2rs, off);
-    qs[3] = buf_ld16(q2rs, off + 2 * gap);
+    const int p = r0 + 16 * w + col;  // rows past S read as zero
+    qs[0] = buf_ld16(q1rs, p * rq1 + 2 * qd0);
+    qs[1] = buf_ld16(q1rs, p * rq1 + 2 * (qd0 + gap));
+    qs[2] = buf_ld16(q2rs, p * rq2 + 2 * qd0);
+    qs[3] = buf_ld16(q2rs, p * rq2 + 2 * (qd0 + gap));
   };
   qload(strip0);
   __syncthreads();
@@ -389,7 +404,7 @@ void diff_band(DiffArgs a, int nblk) {
     band_branch<NKB, NR>(K2s, Vs, s0, Q2, band, edge, jbase, S, a.c, col, grp, ones, O2, l2);
     if (p < S) {
       const float i1 = __builtin_amdgcn_rcpf(l1), i2 = lam * __builtin_amdgcn_rcpf(l2);
-      unsigned short* orow = a.o + base + (size_t)p * HD;
+      unsigned short* orow = oslice + (size_t)p * a.st[TO];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 r;
@@ -417,11 +432,12 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   const int cc = threadIdx.x & 3;
   if (row >= nrows) return;  // whole quads: the four lanes of a row leave together
   const int j = (int)(row % (size_t)a.S);
+  const size_t h = (row / a.S) % a.H, bb = row / a.S / a.H;
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), d0 = lo_dim(cc, rot32);
   float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
-  load_pairs(a.k1 + row * HD, d0, gap, true, k1lo, k1hi);
-  load_pairs(a.k2 + row * HD, d0, gap, true, k2lo, k2hi);
+  load_pairs(a.k1 + slice_at(a, TK1, bb, h) + (size_t)j * a.st[TK1], d0, gap, true, k1lo, k1hi);
+  load_pairs(a.k2 + slice_at(a, TK2, bb, h) + (size_t)j * a.st[TK2], d0, gap, true, k2lo, k2hi);
   prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, sp);
   _Float16* w1 = a.ws + row * HD;
   _Float16* w2 = a.ws + nrows * HD + row * HD;
@@ -430,9 +446,10 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   st16(w2 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2lo)));
   st16(w2 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2hi)));
   if (a.v_keep) {  // V with the rows of flagged-out tokens zeroed, for pass 2
-    const unsigned m = a.v_keep[(row / a.S / a.H) * a.S + j] != 0 ? ~0u : 0u;
+    const unsigned m = a.v_keep[bb * a.S + j] != 0 ? ~0u : 0u;
     unsigned short* w3 = reinterpret_cast<unsigned short*>(a.ws) + 2 * nrows * HD + row * HD;
-    const uint4 x0 = ld16(a.v + row * HD + 16 * cc), x1 = ld16(a.v + row * HD + 16 * cc + 8);
+    const unsigned short* vr = a.v + slice_at(a, TV, bb, h) + (size_t)j * a.st[TV];
+    const uint4 x0 = ld16(vr + 16 * cc), x1 = ld16(vr + 16 * cc + 8);
     st16(w3 + 16 * cc, make_uint4(x0.x & m, x0.y & m, x0.z & m, x0.w & m));
     st16(w3 + 16 * cc + 8, make_uint4(x1.x & m, x1.y & m, x1.z & m, x1.w & m));
   }
@@ -558,7 +575,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int S = a.S, window = a.window;
   const size_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
-  const size_t base = bh * (size_t)S * HD;
+  const size_t bb = bh / a.H;
+  const size_t base = bh * (size_t)S * HD;  // of the workspace's contiguous planes
   const size_t nrows = (size_t)a.B * a.H * S;
   const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
   const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
@@ -574,9 +592,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int i = 0; i < NQB; ++i) {
     const int p = q0 + 16 * i + col;
     float q1lo[8], q1hi[8], q2lo[8], q2hi[8];
-    const size_t po = p < S ? (size_t)p * HD : 0;
-    load_pairs(a.q1 + base + po, qd0, gap, p < S, q1lo, q1hi);
-    load_pairs(a.q2 + base + po, qd0, gap, p < S, q2lo, q2hi);
+    const size_t pc = p < S ? p : 0;
+    load_pairs(a.q1 + slice_at(a, TQ1, bb, h) + pc * a.st[TQ1], qd0, gap, p < S, q1lo, q1hi);
+    load_pairs(a.q2 + slice_at(a, TQ2, bb, h) + pc * a.st[TQ2], qd0, gap, p < S, q2lo, q2hi);
     prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, sp);
     Q1[i][0] = to_f16x8(q1lo);
     Q1[i][1] = to_f16x8(q1hi);
@@ -604,13 +622,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   const int T = t_hi - t_lo + 1;
   const int rbytes = S * HD * 2;
-  // with V flags the values come from the masked copy pass 1 wrote
-  const unsigned short* vsrc = a.v_keep ? reinterpret_cast<const unsigned short*>(a.ws) + 2 * nrows * HD : a.v;
-  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(vsrc + base, rbytes);
+  // with V flags the values come from the masked copy pass 1 wrote (contiguous), else from v
+  const unsigned short* vsrc =
+      a.v_keep ? reinterpret_cast<const unsigned short*>(a.ws) + 2 * nrows * HD + base : a.v + slice_at(a, TV, bb, h);
+  const int vrowb = a.v_keep ? HD * 2 : 2 * a.st[TV];
+  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes);
+  const rsrc_t vrs = make_rsrc(vsrc, a.v_keep ? rbytes : slice_bytes(a, TV));
   uint4 r1[CPT], r2[CPT], rv[CPT];
-  auto gload = [&](const rsrc_t& src, int u, uint4 (&r)[CPT]) {
+  // chunk idx of a tile: row idx / 8, 16-byte column idx % 8; rowb = bytes per row of the source
+  auto gload = [&](const rsrc_t& src, int u, uint4 (&r)[CPT], int rowb) {
 #pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) r[ch] = buf_ld16(src, (t_lo + u) * (DBN * HD * 2) + (tid + ch * NT) * 16);
+    for (int ch = 0; ch < CPT; ++ch) {
+      const int idx = tid + ch * NT;
+      r[ch] = buf_ld16(src, ((t_lo + u) * DBN + (idx >> 3)) * rowb + (idx & 7) * 16);
+    }
   };
   auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
 #pragma unroll
@@ -621,16 +646,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   f32x4 S1a[4][NQB], S1b[4][NQB], S2a[4][NQB], S2b[4][NQB];
-  gload(k1rs, 0, r1);
-  gload(k2rs, 0, r2);
+  gload(k1rs, 0, r1, HD * 2);
+  gload(k2rs, 0, r2, HD * 2);
   swrite(K1b[0], KPD, r1);
   swrite(K2b[0], KPD, r2);
   __syncthreads();
   dpipe_qk<NQB>(K1b[0], Q1, col, grp, S1a);
   dpipe_qk<NQB>(K2b[0], Q2, col, grp, S2a);
   if (T > 1) {
-    gload(k1rs, 1, r1);
-    gload(k2rs, 1, r2);
+    gload(k1rs, 1, r1, HD * 2);
+    gload(k2rs, 1, r2, HD * 2);
     swrite(K1b[1], KPD, r1);
     swrite(K2b[1], KPD, r2);
   }
@@ -642,10 +667,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
     if (NEXT) {
-      gload(k1rs, u + 2, r1);  // past the last tile: zeros, never written
-      gload(k2rs, u + 2, r2);
+      gload(k1rs, u + 2, r1, HD * 2);  // past the last tile: zeros, never written
+      gload(k2rs, u + 2, r2, HD * 2);
     }
-    gload(vrs, u, rv);
+    gload(vrs, u, rv, vrowb);
     if (NEXT) {
       dpipe_qk<NQB>(K1b[(u + 1) & 1], Q1, col, grp, S1n);
       dpipe_qk<NQB>(K2b[(u + 1) & 1], Q2, col, grp, S2n);
@@ -709,7 +734,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float i1 = 1.0f / R.L1[i][0];
     const float i2 = lam / R.L2[i][0];
     if (p < S) {
-      unsigned short* orow = a.o + base + (size_t)p * HD;
+      unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 r;

@@ -33,6 +33,10 @@ struct DiffArgs {
   float rms_eps;
   int rot32;               // 1: rotary on dims 0..31 (pairs i, i+16), dims 32..63 unrotated
   int B, H, S;
+  // element strides of q1, k1, q2, k2, v, o (in that order) as [B][H][S][64] views: batch,
+  // head and token; the 64 dims of a token are contiguous
+  long long sb[6], sh[6];
+  int st[6];
   int window;              // >= 0: |i - j| <= window; < 0: all keys
   float c;                 // scale * log2(e)
   double rev[32];          // revolutions per position of pair i: rope_base^(-2i/64) / (2 pi), or with

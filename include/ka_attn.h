@@ -112,6 +112,12 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
 /* Q/K normaliser of ka_diffattn_fwd_ex. */
 typedef enum { KA_QKNORM_DYT = 0, KA_QKNORM_RMS = 1 } ka_qknorm;
 
+/* Element strides of a [B][H][S][64] bf16 view: element (b, h, s, d) sits at
+ * base + b*batch + h*head + s*token + d.  The 64 dims of a token are contiguous. */
+typedef struct {
+  int64_t batch, head, token;
+} ka_layout;
+
 /*
  * Differential attention in the Stable Audio 3 model's own forms
  * ("401 -> 163 ms: Stable Audio 3 medium on one TPU v6e chip", appendix D1, D3,
@@ -128,6 +134,15 @@ typedef enum { KA_QKNORM_DYT = 0, KA_QKNORM_RMS = 1 } ka_qknorm;
  *   v_keep        NULL (every token kept), or [B][S] bytes on the device: a token
  *                 whose byte is 0 contributes a zero V row; its key stays in both
  *                 softmaxes (the model's padding mask, unlike key masking).
+ *   layouts       NULL (every tensor contiguous [B][H][S][64]), or 6 views in the
+ *                 order q1, k1, q2, k2, v, o, so that q1..v can be read straight out
+ *                 of a fused projection (e.g. [B][S][5][H][64]: token = 5*H*64,
+ *                 head = 64) and o written merged ([B][S][H][64]), with no transposes
+ *                 ("401 -> 163 ms...", appendix E1 "No transposes", D3).  Each stride
+ *                 is a non-negative multiple of 8, token >= 64, and one (b, h) slice
+ *                 spans under 2^31 bytes (else KA_ERR_SHAPE); o's rows must not
+ *                 overlap each other (KA_ERR_SHAPE) nor any input's extent, the span
+ *                 from its base to its last row (KA_ERR_ALIAS).  Inputs may share memory.
  * Everything else -- shapes, dtype, window, lambda, workspace, errors -- is as for
  * ka_diffattn_fwd; rotary_dims other than 32 or 64, or a non-positive or
  * non-finite rms_eps, give KA_ERR_PARAM; an unknown qk_norm KA_ERR_UNSUPPORTED.
@@ -136,8 +151,9 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
                              const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
                              ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
                              const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
-                             float rope_base, const float* lambda, const uint8_t* v_keep, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             float rope_base, const float* lambda, const uint8_t* v_keep,
+                             const ka_layout* layouts, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Workspace bytes ka_diffattn_fwd and ka_diffattn_fwd_ex need for this shape: 0 for
  * the banded path; for the full path the prepared keys (2*B*H*S*64 fp16) plus room

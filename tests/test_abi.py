@@ -118,10 +118,10 @@ KEEP = 0x100000 * 12
 
 def diff_ex(lib, dt=ka.KA_BF16, q1=Q, k1=K, q2=V, k2=O2, v=A, o=O, B=1, H=2, Sq=8, Sk=8, D=64, scale=0.125,
             window=2, norm=ka.KA_QKNORM_RMS, alpha=0, gamma=0, beta=0, rms_w=G, eps=1e-6, rot=32, base=10000.0,
-            lam=L, keep=KEEP, ws=0, ws_bytes=0):
+            lam=L, keep=KEEP, layouts=None, ws=0, ws_bytes=0):
     return lib.ka_diffattn_fwd_ex(dt, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, ctypes.c_float(scale), window, norm,
                                   alpha, gamma, beta, rms_w, ctypes.c_float(eps), rot, ctypes.c_float(base), lam,
-                                  keep, ws, ws_bytes, None)
+                                  keep, layouts, ws, ws_bytes, None)
 
 
 def test_diff_ex_validation(lib):
@@ -143,6 +143,30 @@ def test_diff_ex_validation(lib):
     need3 = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
     assert diff_ex(lib, window=-1, ws=W, ws_bytes=need3 - 1) == _lib.KA_ERR_WORKSPACE
     assert diff_ex(lib, window=-1, ws=KEEP - need3 + 16, ws_bytes=need3) == _lib.KA_ERR_ALIAS
+    assert lib.ka_last_hip_error() == 0
+
+
+def _views(**over):
+    """Six ka_layout views (q1, k1, q2, k2, v, o) for B=1, H=2, S=8, contiguous unless overridden."""
+    base = (2 * 8 * 64, 8 * 64, 64)
+    arr = (_lib.KaLayout * 6)(*[_lib.KaLayout(*over.get(n, base)) for n in ("q1", "k1", "q2", "k2", "v", "o")])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_diff_ex_layout_validation(lib):
+    # a fused projection [B][S][5][H][64]: token stride 5*H*64, head stride 64; merged output [B][S][H][64]
+    fused = (8 * 5 * 2 * 64, 64, 5 * 2 * 64)
+    ok = dict(q1=fused, k1=fused, q2=fused, k2=fused, v=fused, o=(8 * 2 * 64, 64, 2 * 64))
+    p, keep_alive = _views(**ok)
+    assert diff_ex(lib, layouts=p, o=Q) == _lib.KA_ERR_ALIAS  # o inside q1's extent
+    for bad in ((0, 0, 32), (512, 64, 60), (512, 4, 64), (-8, 64, 64)):
+        p, keep_alive = _views(**dict(ok, k2=bad))
+        assert diff_ex(lib, layouts=p) == _lib.KA_ERR_SHAPE, bad
+    p, keep_alive = _views(**dict(ok, o=(1024, 0, 64)))  # the two heads of o on the same rows
+    assert diff_ex(lib, layouts=p) == _lib.KA_ERR_SHAPE
+    p, keep_alive = _views(**dict(ok, v=(1024, 512, 1 << 28)))  # one slice past 32-bit offsets
+    assert diff_ex(lib, layouts=p) == _lib.KA_ERR_SHAPE
+    del keep_alive
     assert lib.ka_last_hip_error() == 0
 
 

@@ -401,3 +401,58 @@ def test_xattn_around_the_on_chip_limit(Sk):
     q, k, v = synth.make_dense(wl, seed_base=1500 + Sk, B=1, H=3, Sq=333, Sk=Sk)
     got = _run_dense(ka.ka_xattn_fwd, q, k, v)
     assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"xattn Sk={Sk}")
+
+
+# ------------------------------------------------------------------ strided views (fused projection in, merged out)
+
+def _fused_views(inputs):
+    """The five [B,H,S,64] inputs laid out as one [B, S, 5, H, 64] projection (sections q1, k1, v, q2,
+    k2, the order of the pages' to_qkv), returned as strided [B,H,S,64] views, and a merged
+    [B, S, H, 64] output viewed as [B,H,S,64]."""
+    q1, k1, q2, k2, v = (to_dev(x) for x in inputs)
+    B, H, S, _ = q1.shape
+    X = torch.stack([t.permute(0, 2, 1, 3) for t in (q1, k1, v, q2, k2)], dim=2).contiguous()  # [B,S,5,H,64]
+    views = [X[:, :, i].permute(0, 2, 1, 3) for i in (0, 1, 3, 4, 2)]  # q1, k1, q2, k2, v
+    out = torch.full((B, S, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    return views, out, out.permute(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("form", ["dyt64", "rms32_padded"])
+@pytest.mark.parametrize("window", [17, 100, -1])
+def test_diff_strided_fused_projection(form, window):
+    S, H, B = 300, 3, 2
+    norm = "rms" if form.startswith("rms") else "dyt"
+    rot = 32 if "32" in form else 64
+    inputs, params = _model_case(norm, S, H, B, 1600 + max(window, 0))
+    keep = synth.make_v_keep(B, S, 29) if "padded" in form else None
+    views, out, o = _fused_views(inputs)
+    assert not views[0].is_contiguous() and not o.is_contiguous()
+    kw = dict(o=o, scale=0.125, window=window, qk_norm=norm, rotary_dims=rot)
+    if norm == "rms":
+        kw.update(rms_weight=to_dev(params[0]), rms_eps=1e-6)
+    else:
+        kw.update(alpha=to_dev(params[0]), gamma=to_dev(params[1]), beta=to_dev(params[2]))
+    if keep is not None:
+        kw["v_keep"] = to_dev(keep)
+    ka.ka_diffattn_fwd_ex(*views, to_dev(params[-1]), **kw)
+    torch.cuda.synchronize()
+    got = to_host_f64(o.contiguous())
+    want = _oracle_diff_ex(inputs, params, window, norm, rot, keep)
+    assert_close(got, want, BF16_TOL, f"strided {form} w={window}")
+    # the same call on contiguous copies gives the same bits
+    assert np.array_equal(got, _run_diff_ex(inputs, params, window, norm, rot, keep))
+
+
+def test_diff_strided_decoder_workload_sampled():
+    """The decoder form reading the fused projection at the banded workload's size."""
+    wl = W["sa3_decoder_banddiff_h8s23086w17"]
+    inputs, params = synth.make_diff(wl)
+    views, out, o = _fused_views(inputs)
+    a, g, b, lm = (to_dev(x) for x in params)
+    ka.ka_diffattn_fwd_ex(*views, lm, o=o, scale=wl.scale, window=wl.window, qk_norm="dyt", alpha=a, gamma=g,
+                          beta=b, rotary_dims=32)
+    torch.cuda.synchronize()
+    got = to_host_f64(o.contiguous()).reshape(-1, D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 1500, 29, edge=40, period=128)
+    want = _oracle_diff_ex(inputs, params, wl.window, "dyt", 32, None, rows=rows, scale=wl.scale)
+    assert_close(got[rows], want, BF16_TOL, "strided decoder form")
