@@ -157,7 +157,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--forms", default="cross,cross_l1,cross_cond257,band,full,band_model,full_model,band_fused",
+    ap.add_argument("--forms", default="cross,cross_l1,cross_cond257,vae_mid,band,full,band_model,full_model,band_fused",
                     help="extra forms to time (comma list, or 'none')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
@@ -244,6 +244,20 @@ def main():
                        "input_copies": len(sets)}
         log(f"bench: {name} {forms[name]}")
         del sets, outs
+    # ---------------- head dim 512: the SDXL VAE's single-head mid-block attention
+    if "vae_mid" in wanted:
+        wl = synth.WORKLOADS["sdxl_vae_mid_b1h1s16384d512"]
+        log(f"bench: {wl.desc}")
+        q5, k5, v5 = (up(x, torch) for x in synth.make_dense(wl))
+        o5 = torch.empty_like(q5)
+        f = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk, D=wl.D)
+        sec = time_launches(lambda i: ka.ka_attn_fwd(q5, k5, v5, o=o5, scale=wl.scale), 1, max(5, args.steps // 5),
+                            args.warmup, torch)
+        forms["vae_mid"] = {"workload": wl.key, "kernel": "attn512_bf16", "us": round(sec * 1e6, 3),
+                            "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
+                            "bound": "mfma", "flops": f}
+        log(f"bench: vae_mid {forms['vae_mid']}")
+        del q5, k5, v5, o5
     # ---------------- banded differential attention (HBM-bound: 3 copies = 425 MB > 256 MB cache)
     if "band" in wanted:
         wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]

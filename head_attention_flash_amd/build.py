@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libka_attn.so")
-SOURCES = ["api.cpp", "attn_dense.hip", "diffattn.hip"]
+SOURCES = ["api.cpp", "attn_dense.hip", "attn512.hip", "diffattn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -22,7 +22,7 @@ COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-t
 
 
 # attention maxima are taken on finite scores or -inf: no IEEE NaN quieting around them
-PER_FILE = {"attn_dense.hip": ["-fno-honor-nans"]}
+PER_FILE = {"attn_dense.hip": ["-fno-honor-nans"], "attn512.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -37,11 +37,12 @@ bool tensor_bytes(int B, int H, int S, int D, size_t elem, size_t* out) {
   return true;
 }
 
+// wide: head dim 512 is accepted (bf16 only)
 ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
-                      int Sk, int D, float scale, size_t* qbytes, size_t* kbytes) {
+                      int Sk, int D, float scale, size_t* qbytes, size_t* kbytes, bool wide = false) {
   if (!q || !k || !v || !o) return KA_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return KA_ERR_SHAPE;
-  if (D != 64) return KA_ERR_UNSUPPORTED;
+  if (D != 64 && !(wide && D == 512 && dt == KA_BF16)) return KA_ERR_UNSUPPORTED;
   if (dt != KA_F32 && dt != KA_BF16) return KA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return KA_ERR_PARAM;
   const size_t e = dt == KA_F32 ? 4 : 2;
@@ -96,8 +97,13 @@ extern "C" {
 ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
                       int Sk, int D, float scale, hipStream_t stream) {
   size_t qb = 0, kb = 0;
-  ka_status st = check_dense(dtype, q, k, v, o, B, H, Sq, Sk, D, scale, &qb, &kb);
+  ka_status st = check_dense(dtype, q, k, v, o, B, H, Sq, Sk, D, scale, &qb, &kb, true);
   if (st != KA_OK) return st;
+  if (D == 512)
+    return hip_status(ka::launch_attn512_bf16(static_cast<const unsigned short*>(q),
+                                              static_cast<const unsigned short*>(k),
+                                              static_cast<const unsigned short*>(v), static_cast<unsigned short*>(o),
+                                              B, H, Sq, Sk, scale, stream));
   if (dtype == KA_F32)
     return hip_status(ka::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                           static_cast<const float*>(v), static_cast<float*>(o), B, H, Sq, Sk, scale,

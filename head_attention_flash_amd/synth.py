@@ -59,6 +59,7 @@ class Workload:
     index: int = 0       # seed namespace
     desc: str = ""
     extra: dict = field(default_factory=dict)
+    D: int = D           # head dim
 
 
 WORKLOADS = {
@@ -73,6 +74,10 @@ WORKLOADS = {
     "sa3_dit_cross_h24q1422k257": Workload("sa3_dit_cross_h24q1422k257", "cross", "bf16", 1, 24, 1422, 257, index=7,
                                            desc="cross-attention to 257 conditioning tokens, DiT-shaped, bf16, "
                                                 "B=1 H=24 Sq=1422 Sk=257"),
+    "sdxl_vae_mid_b1h1s16384d512": Workload("sdxl_vae_mid_b1h1s16384d512", "dense", "bf16", 1, 1, 16384, 16384,
+                                            scale=512 ** -0.5, index=8, D=512,
+                                            desc="SDXL VAE mid-block attention (128x128 latent, one head of 512 "
+                                                 "channels), bf16, B=1 H=1 S=16384 D=512"),
     "sa3_decoder_banddiff_h8s23086w17": Workload("sa3_decoder_banddiff_h8s23086w17", "diff", "bf16", 1, 8, 23086,
                                                  23086, window=17, index=4,
                                                  desc="banded differential attention, decoder-shaped, bf16, "
@@ -91,9 +96,9 @@ def make_dense(wl: Workload, seed_base: int | None = None, Sq: int | None = None
     H = wl.H if H is None else H
     Sq = wl.Sq if Sq is None else Sq
     Sk = wl.Sk if Sk is None else Sk
-    q = normal(base + 0, (B, H, Sq, D), wl.dtype)
-    k = normal(base + 1, (B, H, Sk, D), wl.dtype)
-    v = normal(base + 2, (B, H, Sk, D), wl.dtype)
+    q = normal(base + 0, (B, H, Sq, wl.D), wl.dtype)
+    k = normal(base + 1, (B, H, Sk, wl.D), wl.dtype)
+    v = normal(base + 2, (B, H, Sk, wl.D), wl.dtype)
     return q, k, v
 
 

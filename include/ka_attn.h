@@ -16,7 +16,8 @@
  *     workspace are DEVICE pointers owned by the caller.  The library never
  *     allocates, frees, synchronises or keeps a pointer after the call returns.
  *   - Every activation tensor is contiguous row-major [B][H][S][D] (D innermost);
- *     o has the layout of q.  D must be 64.
+ *     o has the layout of q (ka_diffattn_fwd_ex also takes strided views).  D is 64
+ *     (ka_attn_fwd also takes 512).
  *   - Data types: KA_F32 (float32 in, float32 out, float32 arithmetic) or
  *     KA_BF16 (bfloat16 in, bfloat16 out; matrix products on bf16/fp16 MFMA with
  *     float32 accumulation; softmax, DyT, rotary embedding and the branch
@@ -46,7 +47,7 @@ typedef enum {
   KA_ERR_NULL = 1,         /* a required pointer is NULL                                  */
   KA_ERR_SHAPE = 2,        /* a dimension < 1, Sq != Sk on the diff path, Sk above the
                               cross-attention limit, or a size overflowing 64 bits        */
-  KA_ERR_UNSUPPORTED = 3,  /* D != 64, or a dtype this entry point does not take          */
+  KA_ERR_UNSUPPORTED = 3,  /* a head dim or dtype this entry point does not take           */
   KA_ERR_PARAM = 4,        /* non-finite or non-positive scale, rope_base <= 1 or not
                               finite                                                      */
   KA_ERR_ALIGN = 5,        /* a tensor pointer is not 16-byte aligned                     */
@@ -67,7 +68,9 @@ typedef enum { KA_F32 = 0, KA_BF16 = 1 } ka_dtype;
  *     o[b,h,i,:] = sum_j softmax_j(scale * <q[b,h,i,:], k[b,h,j,:]>) v[b,h,j,:]
  * with j over [0, Sk).  SDXL uses scale = 64^-1/2 = 0.125.
  *   q [B,H,Sq,D], k and v [B,H,Sk,D], o [B,H,Sq,D]; dtype KA_F32 or KA_BF16.
- *   Any B, H, Sq, Sk >= 1.
+ *   Any B, H, Sq, Sk >= 1.  D = 64; or D = 512 with KA_BF16 (the SDXL VAE's
+ *   single-head mid-block attention, 512 channels over 128 x 128 tokens,
+ *   "SDXL as a requirements inventory" s1.5 and s5.10).
  */
 ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
                       int Sk, int D, float scale, hipStream_t stream);

@@ -68,6 +68,17 @@ def pin_dense_vs_torch_sdpa(ora):
         _close(ora.attn(q, k, v, scale), ref, 1e-12, "sdpa")
 
 
+def pin_dense_d512_vs_torch_sdpa(ora):
+    """Head dim 512 (the SDXL VAE's single-head AttnBlock, "SDXL as a requirements inventory" s1.5, s5.10):
+    the same definition, against torch's float64 SDPA at scale 512^-1/2."""
+    r = _rng(3)
+    for (B, H, Sq, Sk) in [(1, 1, 37, 53), (2, 1, 16, 100)]:
+        q, k, v = (r.standard_normal((B, H, s, 512)) for s in (Sq, Sk, Sk))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k).contiguous(), torch.from_numpy(v), scale=512 ** -0.5).numpy()
+        _close(ora.attn(q, k, v, 512 ** -0.5), ref, 1e-12, "sdpa d512")
+
+
 def pin_onehot_v_gives_softmax_rows(ora):
     """V = identity rows: output row i is the softmax row (sums to 1, >= 0, zero past Sk)."""
     r = _rng(2)

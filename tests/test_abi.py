@@ -66,6 +66,7 @@ def test_dense_validation(lib, fn):
     assert dense(lib, fn, Sq=0) == _lib.KA_ERR_SHAPE
     assert dense(lib, fn, Sk=0) == _lib.KA_ERR_SHAPE
     assert dense(lib, fn, D=128) == _lib.KA_ERR_UNSUPPORTED
+    assert dense(lib, fn, D=512, dt=ka.KA_F32) == _lib.KA_ERR_UNSUPPORTED
     assert dense(lib, fn, dt=7) == _lib.KA_ERR_UNSUPPORTED
     assert dense(lib, fn, scale=float("nan")) == _lib.KA_ERR_PARAM
     assert dense(lib, fn, scale=math.inf) == _lib.KA_ERR_PARAM
@@ -76,6 +77,12 @@ def test_dense_validation(lib, fn):
     assert dense(lib, fn, o=K + 256) == _lib.KA_ERR_ALIAS
     assert dense(lib, fn, B=1 << 20, H=1 << 20, Sq=1 << 20) == _lib.KA_ERR_SHAPE  # bytes overflow
     assert lib.ka_last_hip_error() == 0
+
+
+def test_head_dim_512(lib):
+    # ka_attn_fwd takes D = 512 in bf16 (validation runs in full: here it stops at the alias check)
+    assert dense(lib, "ka_attn_fwd", D=512, o=Q) == _lib.KA_ERR_ALIAS
+    assert dense(lib, "ka_xattn_fwd", D=512) == _lib.KA_ERR_UNSUPPORTED
 
 
 def test_xattn_takes_long_key_sets(lib):

@@ -456,3 +456,22 @@ def test_diff_strided_decoder_workload_sampled():
     rows = _rows_sample(wl.B, wl.H, wl.Sq, 1500, 29, edge=40, period=128)
     want = _oracle_diff_ex(inputs, params, wl.window, "dyt", 32, None, rows=rows, scale=wl.scale)
     assert_close(got[rows], want, BF16_TOL, "strided decoder form")
+
+
+# ------------------------------------------------------------------ head dim 512 (SDXL VAE mid-block attention)
+
+@pytest.mark.parametrize("B,H,Sq,Sk", [(1, 1, 300, 333), (2, 2, 64, 31), (1, 1, 1, 1), (1, 3, 130, 64),
+                                       (1, 1, 65, 1000)])
+def test_dense_d512_shapes(B, H, Sq, Sk):
+    wl = W["sdxl_vae_mid_b1h1s16384d512"]
+    q, k, v = synth.make_dense(wl, seed_base=1700 + Sq + Sk, B=B, H=H, Sq=Sq, Sk=Sk)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale)
+    assert_close(got, oracle.attn(q, k, v, wl.scale), BF16_TOL, f"d512 {B}x{H}x{Sq}x{Sk}")
+
+
+def test_dense_d512_vae_workload_sampled():
+    wl = W["sdxl_vae_mid_b1h1s16384d512"]
+    q, k, v = synth.make_dense(wl)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale).reshape(-1, wl.D)
+    rows = _rows_sample(wl.B, wl.H, wl.Sq, 600, 31, edge=8, period=64)
+    assert_close(got[rows], oracle.attn(q, k, v, wl.scale, rows=rows), BF16_TOL, wl.key)
