@@ -22,7 +22,9 @@ COMMON = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-t
 
 
 # attention maxima are taken on finite scores or -inf: no IEEE NaN quieting around them
-PER_FILE = {"attn_dense.hip": ["-fno-honor-nans"], "attn512.hip": ["-fno-honor-nans"]}
+# attn512: matrix accumulators in VGPRs (O and Q^T fit 256 of them), not AGPRs copied back and forth
+PER_FILE = {"attn_dense.hip": ["-fno-honor-nans"],
+            "attn512.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

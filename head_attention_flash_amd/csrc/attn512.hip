@@ -6,11 +6,14 @@
 // v_mfma_f32_16x16x32_bf16 with the softmax statistics of a query in one lane group,
 // with everything eight times wider in D:
 //   - a wave owns 16 queries: its Q^T operand is 16 k-steps of 32 dims (64 VGPRs) and
-//     its O^T accumulator 32 tiles of 16 dims (128 registers, which the compiler keeps
-//     in AGPRs);
+//     its O^T accumulator 32 tiles of 16 dims (128 VGPRs: this file is built with the
+//     matrix instructions' VGPR form, since AGPR accumulators were copied to VGPRs and
+//     back every tile for the rescale);
 //   - a block of four waves (64 queries) shares 32-key K and V tiles of 32 KB each in
-//     LDS, double-buffered (134 KB: one block per CU); each thread stages 8 + 8 chunks
-//     of 16 bytes per tile through registers, loaded one tile ahead;
+//     LDS, double-buffered (134 KB: one block per CU).  Tiles go from HBM straight into
+//     LDS (global_load_lds_dwordx4: one wave instruction moves one 1 KB row, lane i's 16
+//     bytes landing at row base + 16 i), issued one tile ahead, so no registers hold
+//     staged data and O and Q^T fit the VGPRs together;
 //   - per 32-key tile a wave issues 32 MFMAs for S^T and 32 (plus one row-sum MFMA) for
 //     O^T; the softmax is 8 exponentials per lane, an eighth of the matrix work's issue
 //     time at D = 64's ratio, so the loop is bound by the matrix core and by the LDS
@@ -25,7 +28,9 @@ constexpr int D5 = 512;           // head dim
 constexpr int BN5 = 32;           // keys per tile
 constexpr int KP5 = D5 + 8;       // LDS pitch of K (elements): rows 4 banks apart for the b128 fragment reads
 constexpr int VP5 = D5 + 16;      // LDS pitch of V (elements), as VP for the transposed reads
-constexpr int CH5 = BN5 * D5 / 8 / 256;  // 16-byte chunks per thread and tensor per tile (8)
+
+// LDS pointer for the direct global-to-LDS loads
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct Lds512 {
   unsigned short K[2][BN5 * KP5];
@@ -41,9 +46,6 @@ void attn512_bf16(const unsigned short* __restrict__ q, const unsigned short* __
   const size_t bh = blockIdx.y;
   const unsigned short* qb = q + bh * (size_t)Sq * D5;
   unsigned short* ob = o + bh * (size_t)Sq * D5;
-  // keys and values past Sk read as zero through the buffer resources (their scores are masked)
-  const rsrc_t krs = make_rsrc(k + bh * (size_t)Sk * D5, Sk * D5 * 2);
-  const rsrc_t vrs = make_rsrc(v + bh * (size_t)Sk * D5, Sk * D5 * 2);
   const int q0 = blockIdx.x * 64 + 16 * w;
 
   // Q^T (B operand): k-step ks covers dims 32 ks + 8 grp .. + 8 of query q0 + col
@@ -66,44 +68,41 @@ void attn512_bf16(const unsigned short* __restrict__ q, const unsigned short* __
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  // tile staging: chunk tid + 256 it is row (tid + 256 it) / 64, 16-byte column (tid & 63)
-  uint4 sk[CH5], sv[CH5];
-  auto gload = [&](int t) {
+  // tile t into LDS buffer `buf`: wave w moves rows w, w + 4, ... of K and of V, one 1 KB row
+  // per instruction; rows past Sk repeat row Sk - 1 (their scores are masked, their weights 0)
+  const unsigned short* kb = k + bh * (size_t)Sk * D5;
+  const unsigned short* vb = v + bh * (size_t)Sk * D5;
+  auto tile_load = [&](int t, int buf) {
 #pragma unroll
-    for (int it = 0; it < CH5; ++it) {
-      const int off = t * (BN5 * D5 * 2) + (tid + 256 * it) * 16;
-      sk[it] = buf_ld16(krs, off);
-      sv[it] = buf_ld16(vrs, off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < CH5; ++it) {
-      const int row = (tid >> 6) + 4 * it, c8 = (tid & 63) * 8;
-      st16(&sm.K[buf][row * KP5 + c8], sk[it]);
-      st16(&sm.V[buf][row * VP5 + c8], sv[it]);
+    for (int i = 0; i < BN5 / 4; ++i) {
+      const int row = w + 4 * i;
+      const size_t j = (size_t)min(t * BN5 + row, Sk - 1);
+      __builtin_amdgcn_global_load_lds(kb + j * D5 + 8 * lane, (lds_void*)&sm.K[buf][row * KP5], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + j * D5 + 8 * lane, (lds_void*)&sm.V[buf][row * VP5], 16, 0, 0);
     }
   };
 
   const int T = (Sk + BN5 - 1) / BN5;
-  gload(0);
-  lstore(0);
+  tile_load(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     const int cur = t & 1;
-    if (t + 1 < T) gload(t + 1);
+    if (t + 1 < T) tile_load(t + 1, cur ^ 1);  // that buffer was last read in step t - 1
     const unsigned short* Kt = sm.K[cur];
     const unsigned short* Vt = sm.V[cur];
-    // S^T for two 16-key blocks, 16 k-steps each (two independent accumulation chains)
-    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // S^T for two 16-key blocks: four independent accumulation chains (even and odd k-steps)
+    f32x4 S4[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                      {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
     for (int ks = 0; ks < D5 / 32; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb + col) * KP5 + 32 * ks + 8 * grp]);
-        S[kb] = mfma_bf16(a, Qf[ks], S[kb]);
+        S4[kb][ks & 1] = mfma_bf16(a, Qf[ks], S4[kb][ks & 1]);
       }
     }
+    f32x4 S[2] = {S4[0][0] + S4[0][1], S4[1][0] + S4[1][1]};
     if ((t + 1) * BN5 > Sk) {  // tail tile (uniform): keys past Sk take no weight
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -138,7 +137,7 @@ void attn512_bf16(const unsigned short* __restrict__ q, const unsigned short* __
       O[db] = mfma_bf16(a, P, O[db]);
     }
     L = mfma_bf16(ones, P, L);
-    if (t + 1 < T) lstore(cur ^ 1);  // that buffer was last read in step t - 1
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile has landed in LDS
     __syncthreads();
   }
 
