@@ -294,7 +294,7 @@ def main():
         sec = time_graph(lambda i: ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=o, scale=wl.scale,
                                                       window=wl.window, workspace=ws),
                          1, args.steps, args.warmup, torch)
-        forms["full_diff"] = {"workload": wl.key, "kernel": "diff_kprep + diff_flash", "us": round(sec * 1e6, 3),
+        forms["full_diff"] = {"workload": wl.key, "kernel": "diff_kprep + diff_flash_split", "us": round(sec * 1e6, 3),
                               "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
                               "GB/s": round(b / sec / 1e9, 1), "bound": "mfma", "flops": f, "bytes": b}
         log(f"bench: full {forms['full_diff']}")
@@ -367,7 +367,7 @@ def main():
                                                          v_keep=keep, workspace=ws),
                          1, args.steps, args.warmup, torch)
         forms["full_diff_model"] = {"workload": wl.key, "options": f"RMSNorm, rotary on 32 of 64 dims, {pad} padded",
-                                    "kernel": "diff_kprep + diff_flash", "us": round(sec * 1e6, 3),
+                                    "kernel": "diff_kprep + diff_flash_split", "us": round(sec * 1e6, 3),
                                     "TFLOP/s": round(f / sec / 1e12, 3),
                                     "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4), "bound": "mfma", "flops": f}
         log(f"bench: full model form {forms['full_diff_model']}")

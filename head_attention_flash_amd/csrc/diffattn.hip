@@ -39,8 +39,9 @@
 //                      (V1 / Session 8: re-preparing K per query block was half the
 //                      kernel's vector work) -- into the fp16 workspace; with V
 //                      flags also V with the flagged-out rows zeroed.
-//   diff_flash<..>     pass 2: q prep in registers, then a pipelined two-branch
-//                      flash loop over 64-key tiles of the prepared keys and V.
+//   diff_flash_split   pass 2: eight waves per 64 queries, one branch per wave; q prep
+//                      in registers, then a pipelined flash loop over 64-key tiles of the
+//                      prepared keys and V; branch 2 is subtracted through LDS at the end.
 #include <type_traits>
 
 #include "ka_common.hpp"
@@ -457,21 +458,12 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
 
 constexpr int DBN = 64;  // keys per tile
 
-// ---------------------------------------------------------------- full path, pass 2: pipelined two-branch flash
+// ---------------------------------------------------------------- full path, pass 2: building blocks
 // The dense kernel's pipelined loop (S(t+1) and P.V(t-1) on the matrix core around the
 // softmax of tile t; buffer loads; row sums from an all-ones MFMA; lazily raised
-// maxima) carried over to two branches: prepared fp16 keys k1^, k2^ against the
-// prepared queries, one V shared by both P.V products (its fragments are read once).
+// maxima) on prepared fp16 keys against the prepared queries, one branch per wave.
 // BAND: keys outside |i - j| <= window are masked and whole tiles outside the band of
 // the workgroup are skipped (windows too wide for the one-pass band kernel).
-template <int NQB>
-struct DPipeRegs {
-  f32x4 O1[4][NQB], O2[4][NQB];
-  f32x4 L1[NQB], L2[NQB];
-  float m1[NQB], m2[NQB];
-  bf16x8 P1[2][NQB], P2[2][NQB];
-};
-
 template <int NQB>
 __device__ __forceinline__ void dpipe_qk(const unsigned short* Kt, const f16x8 (&Qf)[NQB][2], int col, int grp,
                                          f32x4 (&S)[4][NQB]) {
@@ -483,30 +475,6 @@ __device__ __forceinline__ void dpipe_qk(const unsigned short* Kt, const f16x8 (
     for (int i = 0; i < NQB; ++i) {
       S[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       S[kb][i] = mfma_f16(a1, Qf[i][1], S[kb][i]);
-    }
-  }
-}
-
-template <int NQB>
-__device__ __forceinline__ void dpipe_pv(const unsigned short* Vt, const bf16x8& ones, int col, int grp,
-                                         DPipeRegs<NQB>& R) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 av = cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) {
-        R.O1[db][i] = mfma_bf16(av, R.P1[ks][i], R.O1[db][i]);
-        R.O2[db][i] = mfma_bf16(av, R.P2[ks][i], R.O2[db][i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      R.L1[i] = mfma_bf16(ones, R.P1[ks][i], R.L1[i]);
-      R.L2[i] = mfma_bf16(ones, R.P2[ks][i], R.L2[i]);
     }
   }
 }
@@ -561,187 +529,189 @@ __device__ __forceinline__ bool dpipe_softmax(f32x4 (&S)[4][NQB], int j0, int Sl
   return any;
 }
 
-template <int NQB, int NW, bool BAND, int NORM>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void diff_flash(DiffArgs a) {
+// ---------------------------------------------------------------- full path, pass 2: one branch per wave
+// Eight waves per block, 64 queries: waves 0-3 run branch 1 and waves 4-7 branch 2 for the
+// same four 16-query blocks, so a wave holds one branch's scores, weights and O (about half
+// the registers of a two-branch wave) and twice as many waves share the work; the block
+// stages K1, K2 and V tiles (one 16-byte chunk of each per thread and tile).  At the end
+// branch-2 waves leave lambda O2 / l2 in LDS and branch-1 waves subtract it.
+template <bool BAND, int NORM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void diff_flash_split(DiffArgs a) {
   __shared__ __align__(16) unsigned short K1b[2][DBN * KPD];
   __shared__ __align__(16) unsigned short K2b[2][DBN * KPD];
   __shared__ __align__(16) unsigned short Vb[2][DBN * VPD];
   __shared__ SharedParams sp;
-  constexpr int NT = 64 * NW;
-  constexpr int CPT = (DBN * 8 + NT - 1) / NT;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  const int br = w >> 2;  // 0: branch 1, 1: branch 2 (wave-uniform)
   const int S = a.S, window = a.window;
   const size_t bh = blockIdx.y;
   const int h = (int)(bh % a.H);
   const size_t bb = bh / a.H;
   const size_t base = bh * (size_t)S * HD;  // of the workspace's contiguous planes
   const size_t nrows = (size_t)a.B * a.H * S;
-  const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
-  const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), qd0 = lo_dim(grp, rot32);
   load_params<NORM>(sp, a);
   __syncthreads();
 
-  const int qblk0 = blockIdx.x * NW * 16 * NQB;
-  const int q0 = qblk0 + w * 16 * NQB;
-  f16x8 Q1[NQB][2], Q2[NQB][2];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int p = q0 + 16 * i + col;
-    float q1lo[8], q1hi[8], q2lo[8], q2hi[8];
+  const int qblk0 = blockIdx.x * 64;
+  const int q0 = qblk0 + 16 * (w & 3);
+  const int p = q0 + col;
+  f16x8 Qf[1][2];
+  {
+    // this branch's query (q1 with set 0, or q2 with set 2); prepared twice over so that the
+    // two-tensor preparation serves one tensor
+    const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
+    const unsigned short* qt = br ? a.q2 : a.q1;
+    float lo[8], hi[8], lo2[8], hi2[8];
     const size_t pc = p < S ? p : 0;
-    load_pairs(a.q1 + slice_at(a, TQ1, bb, h) + pc * a.st[TQ1], qd0, gap, p < S, q1lo, q1hi);
-    load_pairs(a.q2 + slice_at(a, TQ2, bb, h) + pc * a.st[TQ2], qd0, gap, p < S, q2lo, q2hi);
-    prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, sp);
-    Q1[i][0] = to_f16x8(q1lo);
-    Q1[i][1] = to_f16x8(q1hi);
-    Q2[i][0] = to_f16x8(q2lo);
-    Q2[i][1] = to_f16x8(q2hi);
-  }
-  DPipeRegs<NQB> R;
+    load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo, hi);
 #pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    R.m1[i] = R.m2[i] = -INFINITY;
-    R.L1[i] = R.L2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < 4; ++db) R.O1[db][i] = R.O2[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 8; ++e) {
+      lo2[e] = lo[e];
+      hi2[e] = hi[e];
+    }
+    prep_pairs2<NORM, RED_GROUP4>(lo, hi, lo2, hi2, qd0, gap, 8 * grp, p, set, set, sp);
+    Qf[0][0] = to_f16x8(lo);
+    Qf[0][1] = to_f16x8(hi);
   }
+  f32x4 O[4], L = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[1] = {-INFINITY};
+  bf16x8 P[2][1];
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  // key tiles this workgroup sees: all, or those touching its band
   int t_lo = 0, t_hi = (S - 1) / DBN;
   if (BAND) {
-    const int qlast = min(S - 1, qblk0 + NW * 16 * NQB - 1);
+    const int qlast = min(S - 1, qblk0 + 63);
     t_lo = max(0, qblk0 - window) / DBN;
     t_hi = min(S - 1, qlast + window) / DBN;
   }
   const int T = t_hi - t_lo + 1;
   const int rbytes = S * HD * 2;
-  // with V flags the values come from the masked copy pass 1 wrote (contiguous), else from v
+  const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
+  const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
   const unsigned short* vsrc =
       a.v_keep ? reinterpret_cast<const unsigned short*>(a.ws) + 2 * nrows * HD + base : a.v + slice_at(a, TV, bb, h);
   const int vrowb = a.v_keep ? HD * 2 : 2 * a.st[TV];
   const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes);
   const rsrc_t vrs = make_rsrc(vsrc, a.v_keep ? rbytes : slice_bytes(a, TV));
-  uint4 r1[CPT], r2[CPT], rv[CPT];
-  // chunk idx of a tile: row idx / 8, 16-byte column idx % 8; rowb = bytes per row of the source
-  auto gload = [&](const rsrc_t& src, int u, uint4 (&r)[CPT], int rowb) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT;
-      r[ch] = buf_ld16(src, ((t_lo + u) * DBN + (idx >> 3)) * rowb + (idx & 7) * 16);
-    }
+  // one chunk per thread and tile: row tid / 8, 16-byte column tid % 8
+  const int srow = tid >> 3, scol = (tid & 7) * 8;
+  auto gld = [&](const rsrc_t& src, int u, int rowb) {
+    return buf_ld16(src, ((t_lo + u) * DBN + srow) * rowb + (tid & 7) * 16);
   };
-  auto swrite = [&](unsigned short* dst, int pitch, const uint4 (&r)[CPT]) {
-#pragma unroll
-    for (int ch = 0; ch < CPT; ++ch) {
-      const int idx = tid + ch * NT, rr = idx >> 3, cc = idx & 7;
-      if (CPT * NT == DBN * 8 || idx < DBN * 8) st16(&dst[rr * pitch + cc * 8], r[ch]);
-    }
-  };
+  unsigned short(*Kr)[DBN * KPD] = br ? K2b : K1b;  // this wave's branch keys
 
-  f32x4 S1a[4][NQB], S1b[4][NQB], S2a[4][NQB], S2b[4][NQB];
-  gload(k1rs, 0, r1, HD * 2);
-  gload(k2rs, 0, r2, HD * 2);
-  swrite(K1b[0], KPD, r1);
-  swrite(K2b[0], KPD, r2);
+  f32x4 Sa[4][1], Sb[4][1];
+  st16(&K1b[0][srow * KPD + scol], gld(k1rs, 0, HD * 2));
+  st16(&K2b[0][srow * KPD + scol], gld(k2rs, 0, HD * 2));
   __syncthreads();
-  dpipe_qk<NQB>(K1b[0], Q1, col, grp, S1a);
-  dpipe_qk<NQB>(K2b[0], Q2, col, grp, S2a);
+  dpipe_qk<1>(Kr[0], Qf, col, grp, Sa);
   if (T > 1) {
-    gload(k1rs, 1, r1, HD * 2);
-    gload(k2rs, 1, r2, HD * 2);
-    swrite(K1b[1], KPD, r1);
-    swrite(K2b[1], KPD, r2);
+    st16(&K1b[1][srow * KPD + scol], gld(k1rs, 1, HD * 2));
+    st16(&K2b[1][srow * KPD + scol], gld(k2rs, 1, HD * 2));
   }
   __syncthreads();
 
-  // step u (tile t_lo + u): S(u+1) and P.V(u-1) on the matrix core, softmax of tile u
-  auto step = [&](auto has_next, auto has_prev, int u, f32x4 (&S1c)[4][NQB], f32x4 (&S1n)[4][NQB],
-                  f32x4 (&S2c)[4][NQB], f32x4 (&S2n)[4][NQB]) {
+  auto step = [&](auto has_next, auto has_prev, int u, f32x4 (&Sc)[4][1], f32x4 (&Sn)[4][1]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
+    uint4 r1, r2;
     if (NEXT) {
-      gload(k1rs, u + 2, r1, HD * 2);  // past the last tile: zeros, never written
-      gload(k2rs, u + 2, r2, HD * 2);
+      r1 = gld(k1rs, u + 2, HD * 2);  // past the last tile: zeros, never written
+      r2 = gld(k2rs, u + 2, HD * 2);
     }
-    gload(vrs, u, rv, vrowb);
-    if (NEXT) {
-      dpipe_qk<NQB>(K1b[(u + 1) & 1], Q1, col, grp, S1n);
-      dpipe_qk<NQB>(K2b[(u + 1) & 1], Q2, col, grp, S2n);
-    }
-    if (PREV) dpipe_pv<NQB>(Vb[(u - 1) & 1], ones, col, grp, R);
-    const int j0 = (t_lo + u) * DBN;
-    const bool tail = j0 + DBN > S;  // uniform
-    float al1[NQB], al2[NQB];
-    bool any;
-    if (tail) {
-      any = dpipe_softmax<NQB, true, BAND>(S1c, j0, S, window, q0, a.c, col, grp, R.m1, al1, R.P1);
-      any |= dpipe_softmax<NQB, true, BAND>(S2c, j0, S, window, q0, a.c, col, grp, R.m2, al2, R.P2);
-    } else {
-      any = dpipe_softmax<NQB, false, BAND>(S1c, j0, S, window, q0, a.c, col, grp, R.m1, al1, R.P1);
-      any |= dpipe_softmax<NQB, false, BAND>(S2c, j0, S, window, q0, a.c, col, grp, R.m2, al2, R.P2);
-    }
-    if (__builtin_amdgcn_ballot_w64(any)) {
+    const uint4 rv = gld(vrs, u, vrowb);
+    if (NEXT) dpipe_qk<1>(Kr[(u + 1) & 1], Qf, col, grp, Sn);
+    if (PREV) {  // P.V of tile u - 1 (one branch) and its row sums
+      const unsigned short* Vt = Vb[(u - 1) & 1];
 #pragma unroll
-      for (int i = 0; i < NQB; ++i) {
+      for (int ks = 0; ks < 2; ++ks) {
+        const int vrow = 32 * ks + 4 * grp + (col >> 2);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          R.O1[db][i] *= al1[i];
-          R.O2[db][i] *= al2[i];
+          const int vcol = 16 * db + 4 * (col & 3);
+          const bf16x8 av =
+              cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
+          O[db] = mfma_bf16(av, P[ks][0], O[db]);
         }
-        R.L1[i] *= al1[i];
-        R.L2[i] *= al2[i];
+        L = mfma_bf16(ones, P[ks][0], L);
       }
     }
-    if (NEXT && u + 2 < T) {
-      swrite(K1b[u & 1], KPD, r1);
-      swrite(K2b[u & 1], KPD, r2);
+    const int j0 = (t_lo + u) * DBN;
+    float al[1];
+    const bool any = j0 + DBN > S ? dpipe_softmax<1, true, BAND>(Sc, j0, S, window, q0, a.c, col, grp, m, al, P)
+                                  : dpipe_softmax<1, false, BAND>(Sc, j0, S, window, q0, a.c, col, grp, m, al, P);
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) O[db] *= al[0];
+      L *= al[0];
     }
-    swrite(Vb[u & 1], VPD, rv);
+    if (NEXT && u + 2 < T) {
+      st16(&K1b[u & 1][srow * KPD + scol], r1);
+      st16(&K2b[u & 1][srow * KPD + scol], r2);
+    }
+    st16(&Vb[u & 1][srow * VPD + scol], rv);
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
-
   if (T == 1) {
-    step(no{}, no{}, 0, S1a, S1b, S2a, S2b);
+    step(no{}, no{}, 0, Sa, Sb);
   } else {
-    step(yes{}, no{}, 0, S1a, S1b, S2a, S2b);
+    step(yes{}, no{}, 0, Sa, Sb);
     int u = 1;
     for (; u + 2 <= T - 1; u += 2) {
-      step(yes{}, yes{}, u, S1b, S1a, S2b, S2a);
-      step(yes{}, yes{}, u + 1, S1a, S1b, S2a, S2b);
+      step(yes{}, yes{}, u, Sb, Sa);
+      step(yes{}, yes{}, u + 1, Sa, Sb);
     }
     if (u < T - 1) {
-      step(yes{}, yes{}, u, S1b, S1a, S2b, S2a);
-      step(no{}, yes{}, u + 1, S1a, S1b, S2a, S2b);
+      step(yes{}, yes{}, u, Sb, Sa);
+      step(no{}, yes{}, u + 1, Sa, Sb);
     } else {
-      step(no{}, yes{}, u, S1b, S1a, S2b, S2a);
+      step(no{}, yes{}, u, Sb, Sa);
     }
   }
-  dpipe_pv<NQB>(Vb[(T - 1) & 1], ones, col, grp, R);
-
-  const float lam = a.lambda[h];
+  {  // P.V of the last tile
+    const unsigned short* Vt = Vb[(T - 1) & 1];
 #pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int p = q0 + 16 * i + col;
-    const float i1 = 1.0f / R.L1[i][0];
-    const float i2 = lam / R.L2[i][0];
-    if (p < S) {
-      unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
+    for (int ks = 0; ks < 2; ++ks) {
+      const int vrow = 32 * ks + 4 * grp + (col >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        f32x4 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = pin(R.O1[db][i][e] * i1) - pin(R.O2[db][i][e] * i2);
-        st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
+        const int vcol = 16 * db + 4 * (col & 3);
+        const bf16x8 av = cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
+        O[db] = mfma_bf16(av, P[ks][0], O[db]);
       }
+      L = mfma_bf16(ones, P[ks][0], L);
+    }
+  }
+  // branch 2 leaves lambda O2 / l2 in LDS (over the K1 tiles, no longer read after the last
+  // barrier); branch 1 subtracts it from O1 / l1
+  f32x4* X = reinterpret_cast<f32x4*>(&K1b[0][0]);  // [4 blocks][4 dim groups][64 lanes]
+  if (br) {
+    const float i2 = a.lambda[h] / L[0];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) X[((w & 3) * 4 + db) * 64 + lane] = f32x4{pin(O[db][0] * i2), pin(O[db][1] * i2),
+                                                                             pin(O[db][2] * i2), pin(O[db][3] * i2)};
+  }
+  __syncthreads();
+  if (!br && p < S) {
+    const float i1 = 1.0f / L[0];
+    unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const f32x4 x = X[((w & 3) * 4 + db) * 64 + lane];
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = pin(O[db][e] * i1) - x[e];
+      st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
     }
   }
 }
@@ -787,18 +757,17 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(diff_kprep<NORM_DYT>, kgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NQB = 1, NW = 4;
-  dim3 grid((a.S + 16 * NQB * NW - 1) / (16 * NQB * NW), BH);
+  dim3 grid((a.S + 63) / 64, BH);
   if (a.norm == NORM_RMS) {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash<NQB, NW, true, NORM_RMS>), grid, dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<true, NORM_RMS>), grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((diff_flash<NQB, NW, false, NORM_RMS>), grid, dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<false, NORM_RMS>), grid, dim3(512), 0, s, a);
   } else {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash<NQB, NW, true, NORM_DYT>), grid, dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<true, NORM_DYT>), grid, dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((diff_flash<NQB, NW, false, NORM_DYT>), grid, dim3(64 * NW), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<false, NORM_DYT>), grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
