@@ -404,7 +404,7 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 // The common 2^-(LAZY_LOG2 - 1) factor of the weights cancels in O / l.
 constexpr int DBN = 32;       // keys per tile
 constexpr int DUO_VSLOT = 5;  // MFMA slot at which a step reads its V fragments
-constexpr int DUO_VLEAD = 2;  // vector work runs this many slots ahead of the MFMAs
+constexpr int DUO_VLEAD = 1;  // vector work runs this many slots ahead of the MFMAs
 constexpr int DUO_STG = 4;    // 4-wave form: vector slot at which the staged K / V are stored
 
 struct DuoLds {
@@ -450,22 +450,17 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     for (int t = 0; t < 2; ++t) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
-      float f[8];
-      unpack_bf16x8(u, f);
-      Qf[i][t] = pack_bf16(f32x4{f[0] * c, f[1] * c, f[2] * c, f[3] * c}, f32x4{f[4] * c, f[5] * c, f[6] * c, f[7] * c});
+      Qf[i][t] = __builtin_bit_cast(bf16x8, u);  // as given: c is applied to each score in fp32
     }
   }
   f32x4 O[4][NQB], L[NQB];
-  // R: exp2-domain reference, LAZY_LOG2 - 1 above the running maximum.  The first QK product of a tile
-  // starts from -R, so scores arrive as c*s - R and the weights 2^(c*s - R) stay below 2 until some score
-  // passes the maximum by LAZY_LOG2: then (and on the first tile) R is raised.
+  // R: exp2-domain reference, LAZY_LOG2 - 1 above the running maximum; the weights 2^(c*s - R) stay
+  // below 2 until some score passes the maximum by LAZY_LOG2: then (and on the first tile) R is raised.
   float R[NQB];
-  f32x4 Bq[NQB];
   bf16x8 P[NQB];
 #pragma unroll
   for (int i = 0; i < NQB; ++i) {
     R[i] = -INFINITY;
-    Bq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < 4; ++db) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -542,7 +537,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       if constexpr (j < NQK) {
         constexpr int i = j / 4, kb = (j / 2) % 2, h = j % 2;
         if constexpr (h == 0)
-          Sn[kb][i] = mfma_bf16(kf[kb][0], Qf[i][0], Bq[i]);
+          Sn[kb][i] = mfma_bf16(kf[kb][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f});
         else
           Sn[kb][i] = mfma_bf16(kf[kb][1], Qf[i][1], Sn[kb][i]);
       } else if constexpr (j < NM) {
@@ -561,7 +556,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       constexpr int i = s / 9, e = s % 9;
       if constexpr (i < NQB) {
         if constexpr (e < 8) {
-          float x = fast_exp2(Sc[e >> 2][i][e & 3]);
+          float x = fast_exp2(__builtin_fmaf(Sc[e >> 2][i][e & 3], c, -R[i]));
           asm volatile("" : "+v"(x));  // computed in its slot, not sunk past the next barrier
           if constexpr (e & 1) {
             Pw[i][e >> 1] = cvt2_bf16(xe[i], x);
@@ -600,21 +595,13 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       for (int i = 0; i < NQB; ++i) {
         const float lmx = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
                                 fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
-        const float base = PREV ? R[i] : 0.f;  // the reference these scores were formed against
-        const float Rn = fmaxf(R[i], base + group4_max(lmx) + (LAZY_LOG2 - 1.f));
+        const float Rn = fmaxf(R[i], __builtin_fmaf(group4_max(lmx), c, LAZY_LOG2 - 1.f));
         const float alpha = fast_exp2(R[i] - Rn);  // 0 on the first tile
-        const float d = Rn - base;
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          Pw[i][h] = cvt2_bf16(fast_exp2(Sc[h >> 1][i][2 * (h & 1)] - d), fast_exp2(Sc[h >> 1][i][2 * (h & 1) + 1] - d));
-        if constexpr (NEXT) {  // the next tile's scores were formed against `base` too
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Sn[kb][i][e] -= d;
-        }
+          Pw[i][h] = cvt2_bf16(fast_exp2(__builtin_fmaf(Sc[h >> 1][i][2 * (h & 1)], c, -Rn)),
+                               fast_exp2(__builtin_fmaf(Sc[h >> 1][i][2 * (h & 1) + 1], c, -Rn)));
         R[i] = Rn;
-        Bq[i] = f32x4{-Rn, -Rn, -Rn, -Rn};
 #pragma unroll
         for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
         L[i] *= alpha;

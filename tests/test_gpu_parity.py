@@ -119,6 +119,26 @@ def test_dense_bf16_workload_sampled():
     assert r["rel_rms"] < 1e-2
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk,qscale", [(1, 20, 4096, 128, 1), (1, 20, 4096, 256, 8), (4, 5, 4096, 384, 1),
+                                             (1, 10, 8192, 640, 8), (2, 10, 4096, 4096, 8)])
+def test_dense_bf16_peaked_large_samples(B, H, Sq, Sk, qscale):
+    """Peaked softmaxes (q scaled by 8: logits with a standard deviation of 8) checked on ~2000
+    sampled rows of 81920: the score scale has to be applied in fp32 (bf16(scale log2(e) q) moved
+    scores by up to 2^-9 of sum |c q_d k_d| and failed the 2e-2 gate here).  Sk = 128, 256, 384
+    give one, two and three key tiles per 128 keys; the grids select the 4-wave unit plan; rows
+    cover every 32-query boundary of some heads."""
+    wl = W["sdxl_l1_self_b2h10s4096"]
+    r = np.random.default_rng(900 + Sk + qscale)
+    q = synth.f32_to_bf16_bits((qscale * r.standard_normal((B, H, Sq, D))).astype(np.float32))
+    k = synth.f32_to_bf16_bits(r.standard_normal((B, H, Sk, D)).astype(np.float32))
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, H, Sk, D)).astype(np.float32))
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale).reshape(-1, D)
+    rows = _rows_sample(B, H, Sq, 400, 17 + Sk, edge=1, period=32)
+    assert_close(got[rows], oracle.attn(q, k, v, wl.scale, rows=rows), BF16_TOL, f"bf16 {B}x{H}x{Sq}x{Sk}")
+    # every row was written (the output started as NaN)
+    assert np.isfinite(got).all()
+
+
 def test_dense_bf16_deterministic():
     wl = W["sdxl_l1_self_b2h10s4096"]
     q, k, v = (to_dev(x) for x in synth.make_dense(wl, B=1, H=3, Sq=1000, Sk=900))
