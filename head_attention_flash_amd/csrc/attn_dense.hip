@@ -390,17 +390,15 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 // then the block synchronises once.  Threads 0-255 stage K, 256-511 stage V, one
 // 16-byte chunk each per tile, loaded one step before it is stored.
 //
-// Vector work is what bounds this loop on CDNA4 (an MFMA hides little of it), so the
-// weights take one v_exp each and nothing else but the bf16 pack:
-//   * Q is held pre-multiplied by c = scale * log2(e) (one bf16 rounding of c*q, at most
-//     2^-9 relative), and each tile's first QK product starts from -R instead of zero,
-//     so the scores arrive as c*s - R and the weight is 2^(score) directly;
+// Vector work is what bounds this loop on CDNA4 (an MFMA hides little of it), so a
+// weight takes one FMA and one v_exp and nothing else but the bf16 pack:
+//   * the weight is 2^(c*s - R), c = scale * log2(e) applied to the fp32 score (Q as
+//     given: a bf16 rounding of c*q would move scores by up to 2^-9 of sum |c q_d k_d|);
 //   * R sits LAZY_LOG2 - 1 above the running maximum, so every weight stays below 2
 //     unless a score passes the maximum by LAZY_LOG2.  Weights >= 2 are the bf16 values
 //     with bit 14 set: one OR over the packed weights and a wave-wide vote replace the
 //     per-tile maximum.  Only on a vote (and on the first tile) are the four-lane maxima
-//     taken, R raised, this tile's weights recomputed, the next tile's scores (already
-//     formed against the old R) shifted, and O, l rescaled.
+//     taken, R raised, this tile's weights recomputed, and O, l rescaled.
 // The common 2^-(LAZY_LOG2 - 1) factor of the weights cancels in O / l.
 constexpr int DBN = 32;       // keys per tile
 constexpr int DUO_VSLOT = 5;  // MFMA slot at which a step reads its V fragments
