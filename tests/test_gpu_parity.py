@@ -489,6 +489,30 @@ def test_dense_d512_shapes(B, H, Sq, Sk):
     assert_close(got, oracle.attn(q, k, v, wl.scale), BF16_TOL, f"d512 {B}x{H}x{Sq}x{Sk}")
 
 
+def _peaked(shape_q, shape_kv, qscale, seed):
+    r = np.random.default_rng(seed)
+    q = synth.f32_to_bf16_bits((qscale * r.standard_normal(shape_q)).astype(np.float32))
+    k = synth.f32_to_bf16_bits(r.standard_normal(shape_kv).astype(np.float32))
+    v = synth.f32_to_bf16_bits(r.standard_normal(shape_kv).astype(np.float32))
+    return q, k, v
+
+
+@pytest.mark.parametrize("Sk", [77, 256, 300])
+def test_xattn_peaked(Sk):
+    """Cross-attention with q scaled by 8 (logit std 8): LDS-resident keys (77, 256) and streamed (300)."""
+    q, k, v = _peaked((2, 4, 700, D), (2, 4, Sk, D), 8, 2100 + Sk)
+    got = _run_dense(ka.ka_xattn_fwd, q, k, v)
+    assert_close(got, oracle.attn(q, k, v, 0.125), BF16_TOL, f"xattn peaked Sk={Sk}")
+
+
+def test_dense_d512_peaked():
+    """Head dim 512 with q scaled by 4 (logit std 4 at scale 512^-1/2)."""
+    wl = W["sdxl_vae_mid_b1h1s16384d512"]
+    q, k, v = _peaked((1, 1, 300, 512), (1, 1, 700, 512), 4, 2200)
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, wl.scale)
+    assert_close(got, oracle.attn(q, k, v, wl.scale), BF16_TOL, "d512 peaked")
+
+
 def test_dense_d512_vae_workload_sampled():
     wl = W["sdxl_vae_mid_b1h1s16384d512"]
     q, k, v = synth.make_dense(wl)
