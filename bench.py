@@ -151,6 +151,27 @@ def cpu_baseline(wl):
             "sample": f"the whole {wl.key} workload ({wl.B * wl.H * wl.Sq} query rows x {wl.Sk} keys), {dt:.2f} s"}
 
 
+def run_env(torch):
+    """What the numbers were measured on: device, CU count, ROCm and torch versions, source revision."""
+    env = {"device": torch.cuda.get_device_name(0),
+           "cus": torch.cuda.get_device_properties(0).multi_processor_count,
+           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        import subprocess
+        here = os.path.dirname(os.path.abspath(__file__))
+        r = subprocess.run(["git", "-C", here, "rev-parse", "--short", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        env["git"] = r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        env["git"] = None
+    return env
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +397,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(synth.WORKLOADS["sdxl_l1_self_b2h10s4096"])
+    result["env"] = run_env(torch)
     print(json.dumps(result), flush=True)
 
 
