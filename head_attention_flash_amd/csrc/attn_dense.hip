@@ -427,7 +427,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
                                          const unsigned short* kbase, const unsigned short* vbase, int Sk, float c,
                                          unsigned short* __restrict__ ob, int tid) {
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const bool isK = QUAD || tid < 256;
+  const bool isK = QUAD || __builtin_amdgcn_readfirstlane(tid >> 6) < 4;  // wave-uniform: a scalar buffer resource
   const int chunk = tid & 255, srow = chunk >> 3, scol = (chunk & 7) * 8;
   // rows past Sk read as zero through the buffer resource
   const rsrc_t srs = make_rsrc(isK ? kbase : vbase, Sk * HD * 2);
