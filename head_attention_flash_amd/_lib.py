@@ -18,11 +18,11 @@ KA_OK, KA_ERR_NULL, KA_ERR_SHAPE, KA_ERR_UNSUPPORTED, KA_ERR_PARAM, KA_ERR_ALIGN
     KA_ERR_WORKSPACE, KA_ERR_HIP = range(9)
 KA_F32, KA_BF16 = 0, 1
 KA_QKNORM_DYT, KA_QKNORM_RMS = 0, 1
-KA_XATTN_MAX_SK = 256
+KA_XATTN_MAX_SK = 512
 
 # every symbol include/ka_attn.h declares
 EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_fwd_ex", "ka_diffattn_workspace_bytes",
-           "ka_status_string", "ka_last_hip_error", "ka_version")
+           "ka_attn_kernel_name", "ka_status_string", "ka_last_hip_error", "ka_version")
 
 
 class KaError(RuntimeError):
@@ -57,6 +57,8 @@ def load(path: str = LIB_PATH):
     lib.ka_diffattn_fwd_ex.restype = i
     lib.ka_diffattn_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.ka_diffattn_workspace_bytes.restype = sz
+    lib.ka_attn_kernel_name.argtypes = [i, i, i, i, i, i]
+    lib.ka_attn_kernel_name.restype = ctypes.c_char_p
     lib.ka_status_string.argtypes = [i]
     lib.ka_status_string.restype = ctypes.c_char_p
     lib.ka_last_hip_error.argtypes = []
@@ -81,6 +83,57 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.bfloat16:
         return KA_BF16
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _expect(t, name: str, shape, dtype, device):
+    """Check a tensor argument's shape, dtype and device before any pointer reaches the C ABI (which
+    sees raw pointers only and cannot tell a short or mistyped buffer from a good one)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the device of the first operand)")
+
+
+def _check_qkv(q, k, v, o):
+    """q [B,H,Sq,D], k and v [B,H,Sk,D], o like q: one dtype (fp32 or bf16), one device."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, Sq, D], got shape {tuple(q.shape)}")
+    _dtype_code(q)
+    if k.dim() != 4:
+        raise ValueError(f"k must be [B, H, Sk, D], got shape {tuple(k.shape)}")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    _expect(k, "k", (B, H, Sk, D), q.dtype, q.device)
+    _expect(v, "v", (B, H, Sk, D), q.dtype, q.device)
+    if o is not None:
+        _expect(o, "o", (B, H, Sq, D), q.dtype, q.device)
+
+
+def _check_diff(q1, k1, q2, k2, v, o, lam, params, v_keep=None, workspace=None):
+    """q1, k1, q2, k2, v, o [B,H,S,64] bf16; lam [H] fp32; params: (name, tensor, shape) of the fp32
+    parameter arrays in use; v_keep [B,S] uint8; workspace a uint8 tensor.  One device."""
+    torch = _torch()
+    if q1.dim() != 4:
+        raise ValueError(f"q1 must be [B, H, S, 64], got shape {tuple(q1.shape)}")
+    B, H, S, D = q1.shape
+    dev = q1.device
+    for t, name in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (o, "o")):
+        if t is not None:
+            _expect(t, name, (B, H, S, D), torch.bfloat16, dev)
+    _expect(lam, "lambda", (H,), torch.float32, dev)
+    for name, t, shape in params:
+        _expect(t, name, shape, torch.float32, dev)
+    if v_keep is not None:
+        _expect(v_keep, "v_keep", (B, S), torch.uint8, dev)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        if workspace.device != dev:
+            raise ValueError(f"workspace is on {workspace.device}, expected {dev}")
 
 
 def _dev(t, name: str):
@@ -120,6 +173,7 @@ def _check(lib, st: int, where: str):
 def ka_attn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
     """Dense attention; q [B,H,Sq,64], k/v [B,H,Sk,64] (fp32 or bf16, same dtype). Returns o."""
     lib = load()
+    _check_qkv(q, k, v, o)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     if o is None:
@@ -133,6 +187,7 @@ def ka_attn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
 def ka_xattn_fwd(q, k, v, o=None, scale: float = 0.125, stream=None):
     """Cross-attention: key sets up to 256 held on chip, longer ones streamed. Returns o."""
     lib = load()
+    _check_qkv(q, k, v, o)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     if o is None:
@@ -147,6 +202,12 @@ def ka_diffattn_workspace_bytes(B: int, H: int, S: int, D: int = 64, window: int
     return int(load().ka_diffattn_workspace_bytes(B, H, S, D, window))
 
 
+def ka_attn_kernel_name(B: int, H: int, Sq: int, Sk: int, D: int = 64, dtype: int = KA_BF16):
+    """Name and layout of the kernel ka_attn_fwd runs for this shape on the current device, or None."""
+    r = load().ka_attn_kernel_name(dtype, B, H, Sq, Sk, D)
+    return r.decode() if r is not None else None
+
+
 def ka_diffattn_fwd(q1, k1, q2, k2, v, alpha, gamma, beta, lam, o=None, scale: float = 0.125, window: int = -1,
                     rope_base: float = 10000.0, workspace=None, stream=None):
     """Differential attention (bf16). alpha [4], gamma/beta [4,64], lam [H]: fp32 GPU tensors.
@@ -155,6 +216,8 @@ def ka_diffattn_fwd(q1, k1, q2, k2, v, alpha, gamma, beta, lam, o=None, scale: f
     have torch allocate one for this call.
     """
     lib = load()
+    _check_diff(q1, k1, q2, k2, v, o, lam, (("alpha", alpha, (4,)), ("gamma", gamma, (4, 64)), ("beta", beta, (4, 64))),
+                workspace=workspace)
     B, H, S, D = q1.shape
     if o is None:
         o = _torch().empty_like(q1)
@@ -181,6 +244,11 @@ def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, win
     their strides are passed as ka_layout views.
     """
     lib = load()
+    if qk_norm not in ("dyt", "rms"):
+        raise ValueError(f"qk_norm must be 'dyt' or 'rms', got {qk_norm!r}")
+    prm = ((("alpha", alpha, (4,)), ("gamma", gamma, (4, 64)), ("beta", beta, (4, 64))) if qk_norm == "dyt"
+           else (("rms_weight", rms_weight, (4, 64)),))
+    _check_diff(q1, k1, q2, k2, v, o, lam, prm, v_keep=v_keep, workspace=workspace)
     B, H, S, D = q1.shape
     if o is None:
         o = _torch().empty_like(q1)
@@ -191,8 +259,6 @@ def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, win
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     norm = {"dyt": KA_QKNORM_DYT, "rms": KA_QKNORM_RMS}[qk_norm]
     opt = lambda t, name: _dev(t, name) if t is not None else ctypes.c_void_p(0)  # noqa: E731
-    if v_keep is not None and v_keep.dtype != _torch().uint8:
-        raise TypeError("v_keep must be a uint8 tensor")
     views = [_dev_view(t, n) for t, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (o, "o"))]
     layouts = None
     if not all(t.is_contiguous() for t in (q1, k1, q2, k2, v, o)):

@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI of libka_attn: validation on the host, then one launch
-// sequence on the caller's stream.  No allocation, no synchronisation, no state
-// beyond a thread-local copy of the last HIP error.
+// sequence on the caller's stream.  No allocation, no synchronisation; the only state
+// is a thread-local copy of the last HIP error (plus, in the launchers, a per-device
+// cache of the CU count kept in atomics and a per-thread cache of the last dense plan).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -21,6 +22,8 @@ ka_status hip_status(hipError_t e) {
   return KA_ERR_HIP;
 }
 
+constexpr size_t HD_ = 64;  // head dim of the differential path and its parameter rows
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // [p, p + n) and [q, q + m) overlap
@@ -37,6 +40,10 @@ bool tensor_bytes(int B, int H, int S, int D, size_t elem, size_t* out) {
   return true;
 }
 
+// B*H*ceil(S/64) < 2^23: the query blocks of 64 rows over all (b, h), the unit every
+// launch's one-dimensional grid is sized by (at most 512 work-items each)
+bool grid_ok(int B, int H, int S) { return (long long)B * H * ((S + 63) / 64) < (1LL << 23); }
+
 // wide: head dim 512 is accepted (bf16 only)
 ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, void* o, int B, int H, int Sq,
                       int Sk, int D, float scale, size_t* qbytes, size_t* kbytes, bool wide = false) {
@@ -47,9 +54,10 @@ ka_status check_dense(ka_dtype dt, const void* q, const void* k, const void* v, 
   if (!std::isfinite(scale) || !(scale > 0.0f)) return KA_ERR_PARAM;
   const size_t e = dt == KA_F32 ? 4 : 2;
   if (!tensor_bytes(B, H, Sq, D, e, qbytes) || !tensor_bytes(B, H, Sk, D, e, kbytes)) return KA_ERR_SHAPE;
-  // grids carry B*H (times the query blocks) in 32 bits; key tiles use 32-bit buffer offsets
-  if ((long long)B * H * ((Sq + 15) / 16) > 0x7fffffffLL) return KA_ERR_SHAPE;
-  if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  // every launch has at most 512 work-items per 64 query rows of a (b, h) and one grid
+  // dimension, so B*H*ceil(Sq/64) below 2^23 keeps its work-item count within 32 bits; key
+  // tiles use 32-bit buffer offsets
+  if (!grid_ok(B, H, Sq)) return KA_ERR_SHAPE;
   if ((long long)Sk * D * (long long)e + 2LL * 64 * D * (long long)e > 0x7fffffffLL) return KA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return KA_ERR_ALIGN;
   if (overlap(o, *qbytes, q, *qbytes) || overlap(o, *qbytes, k, *kbytes) || overlap(o, *qbytes, v, *kbytes))
@@ -156,7 +164,7 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
   const int S = Sq;
   size_t tb = 0;
   if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
-  if ((long long)B * H > 65535LL * 1024) return KA_ERR_SHAPE;
+  if (!grid_ok(B, H, S)) return KA_ERR_SHAPE;
   // views of q1, k1, q2, k2, v, o: the given strides, or contiguous [B][H][S][64]
   ka_layout lay[6];
   size_t ext[6];
@@ -186,6 +194,20 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
     const size_t nk = (size_t)B * S;
     if (overlap(o, ext[5], v_keep, nk) || (need && overlap(workspace, need, v_keep, nk))) return KA_ERR_ALIAS;
   }
+  // the parameter arrays are read by every workgroup while others write o and the workspace
+  const void* prm[4] = {dyt_alpha, dyt_gamma, dyt_beta, rms_weight};
+  const size_t prm_bytes[4] = {4 * sizeof(float), 4 * HD_ * sizeof(float), 4 * HD_ * sizeof(float),
+                               4 * HD_ * sizeof(float)};
+  const bool prm_used[4] = {qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT,
+                            qk_norm == KA_QKNORM_RMS};
+  for (int t = 0; t < 4; ++t) {
+    if (!prm_used[t]) continue;
+    if (overlap(o, ext[5], prm[t], prm_bytes[t]) || (need && overlap(workspace, need, prm[t], prm_bytes[t])))
+      return KA_ERR_ALIAS;
+  }
+  if (overlap(o, ext[5], lambda, (size_t)H * sizeof(float)) ||
+      (need && overlap(workspace, need, lambda, (size_t)H * sizeof(float))))
+    return KA_ERR_ALIAS;
 
   ka::DiffArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -246,6 +268,15 @@ ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const 
   return ka_diffattn_fwd_ex(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, KA_QKNORM_DYT, dyt_alpha,
                             dyt_gamma, dyt_beta, nullptr, 1.0f, 64, rope_base, lambda, nullptr, nullptr, workspace,
                             workspace_bytes, stream);
+}
+
+const char* ka_attn_kernel_name(ka_dtype dtype, int B, int H, int Sq, int Sk, int D) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || !grid_ok(B, H, Sq)) return nullptr;
+  if (dtype == KA_F32 && D == 64) return "attn_f32";
+  if (dtype != KA_BF16) return nullptr;
+  if (D == 512) return "attn512_bf16";
+  if (D != 64) return nullptr;
+  return ka::attn_bf16_kernel_name(B, H, Sq);
 }
 
 const char* ka_status_string(ka_status s) {

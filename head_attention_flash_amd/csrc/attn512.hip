@@ -39,14 +39,15 @@ struct Lds512 {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn512_bf16(const unsigned short* __restrict__ q, const unsigned short* __restrict__ k,
-                  const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c) {
+                  const unsigned short* __restrict__ v, unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                  int nqb) {
   __shared__ __align__(16) Lds512 sm;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const size_t bh = blockIdx.y;
+  const size_t bh = blockIdx.x / nqb;  // one-dimensional grid: (b, h) major, 64-query block minor
   const unsigned short* qb = q + bh * (size_t)Sq * D5;
   unsigned short* ob = o + bh * (size_t)Sq * D5;
-  const int q0 = blockIdx.x * 64 + 16 * w;
+  const int q0 = (blockIdx.x % nqb) * 64 + 16 * w;
 
   // Q^T (B operand): k-step ks covers dims 32 ks + 8 grp .. + 8 of query q0 + col
   bf16x8 Qf[D5 / 32];
@@ -153,8 +154,8 @@ void attn512_bf16(const unsigned short* __restrict__ q, const unsigned short* __
 
 hipError_t launch_attn512_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                                unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
-  dim3 grid((Sq + 63) / 64, B * H);
-  hipLaunchKernelGGL(attn512_bf16, grid, dim3(256), 0, s, q, k, v, o, Sq, Sk, scale * LOG2E);
+  const int nqb = (Sq + 63) / 64;
+  hipLaunchKernelGGL(attn512_bf16, dim3(nqb * B * H), dim3(256), 0, s, q, k, v, o, Sq, Sk, scale * LOG2E, nqb);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@
 // This file is compiled without NaN semantics (-fno-honor-nans): the maxima are
 // taken on finite scores or -inf, and IEEE NaN quieting would double their cost.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -48,12 +49,12 @@ constexpr int F32_BK = 32;   // keys per LDS tile
 
 __global__ __launch_bounds__(F32_BQ) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                           const float* __restrict__ v, float* __restrict__ o, int Sq,
-                                                          int Sk, float scale) {
+                                                          int Sk, float scale, int nqb) {
   __shared__ __align__(16) float ks[F32_BK][HD];
   __shared__ __align__(16) float vs[F32_BK][HD];
   const int tid = threadIdx.x;
-  const size_t bh = blockIdx.y;
-  const int i = blockIdx.x * F32_BQ + tid;
+  const size_t bh = blockIdx.x / nqb;  // one-dimensional grid: (b, h) major, query block minor
+  const int i = (blockIdx.x % nqb) * F32_BQ + tid;
   const float* qb = q + bh * (size_t)Sq * HD;
   const float* kb = k + bh * (size_t)Sk * HD;
   const float* vb = v + bh * (size_t)Sk * HD;
@@ -548,7 +549,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     };
     unsigned Pw[NQB][4];
     float xe[NQB];
-    unsigned orb = 0;
+    unsigned orb[NQB];
     auto valu_at = [&](auto ss) {
       constexpr int s = decltype(ss)::value;
       constexpr int i = s / 9, e = s % 9;
@@ -563,7 +564,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
             xe[i] = x;
           }
         } else {
-          orb |= Pw[i][0] | Pw[i][1] | Pw[i][2] | Pw[i][3];
+          orb[i] = Pw[i][0] | Pw[i][1] | Pw[i][2] | Pw[i][3];
         }
       }
     };
@@ -587,14 +588,21 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       }(), ...);
     }(std::make_integer_sequence<int, NSLOT>{});
     // some weight of this tile reached 2 (bit 14 of a bf16 half), or first tile
-    const bool raised = !PREV || __builtin_amdgcn_ballot_w64((orb & 0x40004000u) != 0) != 0;
+    unsigned orall = 0;
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) orall |= orb[i];
+    const bool raised = !PREV || __builtin_amdgcn_ballot_w64((orall & 0x40004000u) != 0) != 0;
     if (raised) {
 #pragma unroll
       for (int i = 0; i < NQB; ++i) {
+        // R moves only for a query whose own largest weight, 2^(c max - R), reached 2 (always on
+        // the first tile, where R = -inf), so a query's result never depends on the other queries
+        // of its wave; every such query is in a wave that voted
         const float lmx = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
                                 fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
-        const float Rn = fmaxf(R[i], __builtin_fmaf(group4_max(lmx), c, LAZY_LOG2 - 1.f));
-        const float alpha = fast_exp2(R[i] - Rn);  // 0 on the first tile
+        const float gmx = group4_max(lmx);
+        const float Rn = __builtin_fmaf(gmx, c, -R[i]) >= 1.0f ? __builtin_fmaf(gmx, c, LAZY_LOG2 - 1.f) : R[i];
+        const float alpha = fast_exp2(R[i] - Rn);  // 0 on the first tile, 1 where R stays
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           Pw[i][h] = cvt2_bf16(fast_exp2(__builtin_fmaf(Sc[h >> 1][i][2 * (h & 1)], c, -Rn)),
@@ -735,131 +743,197 @@ void attn_bf16_quad(const unsigned short* __restrict__ q, const unsigned short* 
 }
 
 // ---------------------------------------------------------------- bf16 cross (keys resident in LDS)
-template <int NKB, int NQB, int NW>
+// Every key and value of a (b, h) is loaded into LDS once per workgroup and re-read by all
+// its query blocks ("SDXL as a requirements inventory" s5.7: hold the re-read operand on
+// chip, stream Q and O).  A workgroup serves a chunk of `qpc` queries of one (b, h): its
+// waves take the chunk's 16-query blocks in turn, each requesting its next block's query
+// rows while the current one computes.  Workgroups are numbered XCD-major so that the
+// workgroups of one (b, h) share one XCD's L2.
+//   ONLINE = false (NK <= 128): all scores of a query block in registers, one exact softmax.
+//   ONLINE = true  (NK <= 512, the LDS budget): 64-key chunks out of LDS with a running
+//   maximum and sum (the online softmax), O rescaled when the maximum rises.
+
+// Workgroups are dispatched round-robin over the 8 XCDs: block b runs on XCD b % 8.  Map the
+// first 8 * floor(n / 8) blocks so that XCD x takes a contiguous run of items.
+__device__ __forceinline__ int xcd_major(int blk, int n) {
+  const int n8 = n & ~7;
+  return blk < n8 ? (blk & 7) * (n8 >> 3) + (blk >> 3) : blk;
+}
+
+template <int NK, int NW, bool ONLINE>
 __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __restrict__ q,
                                                       const unsigned short* __restrict__ k,
                                                       const unsigned short* __restrict__ v,
-                                                      unsigned short* __restrict__ o, int Sq, int Sk, float c) {
-  static_assert(NKB % 2 == 0, "keys are consumed in 32-key steps");
-  constexpr int NK = 16 * NKB;
+                                                      unsigned short* __restrict__ o, int Sq, int Sk, float c,
+                                                      int nchunk, int qpc) {
+  static_assert(NK % (ONLINE ? 64 : 32) == 0, "keys are consumed in 32-key (64-key online) steps");
+  constexpr int NKB = NK / 16;
   __shared__ __align__(16) unsigned short Ks[NK * KP];
   __shared__ __align__(16) unsigned short Vs[NK * VP];
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const size_t bh = blockIdx.y;
-  const unsigned short* kb = k + bh * (size_t)Sk * HD;
-  const unsigned short* vb = v + bh * (size_t)Sk * HD;
-
-  // All loads are issued before the first LDS store, so that the latencies of this wave's
-  // query rows and of every key/value chunk overlap instead of following one another.
-  const int q0 = (blockIdx.x * NW + w) * (16 * NQB);
+  const int item = xcd_major(blockIdx.x, gridDim.x);
+  const size_t bh = item / nchunk;
+  const int qbase = (item % nchunk) * qpc;                  // qpc: a multiple of 16
+  const int qend = min(Sq, qbase + qpc);
   const unsigned short* qb = q + bh * (size_t)Sq * HD;
-  bf16x8 Qf[NQB][2];
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const int row = q0 + 16 * i + col;
+  unsigned short* ob = o + bh * (size_t)Sq * HD;
+
+  // this wave's query rows of its i-th block: qbase + 16 (i NW + w) + col; rows past Sq read as zero
+  auto qload = [&](int i, bf16x8 (&Qf)[2]) {
+    const int row = qbase + 16 * (i * NW + w) + col;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint4 u = make_uint4(0, 0, 0, 0);
       if (row < Sq) u = ld16(qb + (size_t)row * HD + 32 * t + 8 * grp);
-      Qf[i][t] = __builtin_bit_cast(bf16x8, u);
+      Qf[t] = __builtin_bit_cast(bf16x8, u);
     }
-  }
-  // every key and value of this (b, h), rows past Sk zero (their scores are masked)
-  constexpr int NIT = (NK * 8 + NT - 1) / NT;
-  uint4 kk[NIT], vv[NIT];
+  };
+  bf16x8 Qc[2], Qn[2];
+  qload(0, Qc);
+  {
+    // every key and value of this (b, h); rows past Sk read as zero through the buffer
+    // resources (their scores are masked)
+    const rsrc_t krs = make_rsrc(k + bh * (size_t)Sk * HD, Sk * HD * 2);
+    const rsrc_t vrs = make_rsrc(v + bh * (size_t)Sk * HD, Sk * HD * 2);
+    constexpr int NIT = (NK * 8 + NT - 1) / NT;
+    uint4 kk[NIT], vv[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int idx = tid + it * NT, r = idx >> 3, cc = idx & 7;
-    kk[it] = vv[it] = make_uint4(0, 0, 0, 0);
-    if (idx < NK * 8 && r < Sk) {
-      kk[it] = ld16(kb + (size_t)r * HD + cc * 8);
-      vv[it] = ld16(vb + (size_t)r * HD + cc * 8);
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NT;
+      kk[it] = buf_ld16(krs, idx * 16);
+      vv[it] = buf_ld16(vrs, idx * 16);
     }
-  }
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int idx = tid + it * NT, r = idx >> 3, cc = idx & 7;
-    if (idx < NK * 8) {
-      st16(&Ks[r * KP + cc * 8], kk[it]);
-      st16(&Vs[r * VP + cc * 8], vv[it]);
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * NT, r = idx >> 3, cc = idx & 7;
+      if (NIT * NT == NK * 8 || idx < NK * 8) {
+        st16(&Ks[r * KP + cc * 8], kk[it]);
+        st16(&Vs[r * VP + cc * 8], vv[it]);
+      }
     }
   }
   __syncthreads();
-  if (q0 >= Sq) return;
 
-  f32x4 S[NKB][NQB];
+  // ONLINE = false: the launcher gives every wave one block (qpc = 16 NW), so there is no loop
+  for (int i = 0; ONLINE || i == 0; ++i) {
+    const int q0 = qbase + 16 * (i * NW + w);
+    if (q0 >= qend) break;  // wave-uniform; later blocks lie further on
+    if (ONLINE && q0 + 16 * NW < qend) qload(i + 1, Qn);
+    f32x4 O[4];
 #pragma unroll
-  for (int kb_ = 0; kb_ < NKB; ++kb_) {
+    for (int db = 0; db < 4; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float l;
+    if constexpr (!ONLINE) {
+      f32x4 S[NKB];
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) S[kb_][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(16 * kb_ + col) * KP + 32 * tt + 8 * grp]);
-#pragma unroll
-      for (int i = 0; i < NQB; ++i) S[kb_][i] = mfma_bf16(a, Qf[i][tt], S[kb_][i]);
-    }
-  }
-  if (Sk < NK) {  // padded keys are set to -inf before the maximum is taken
-#pragma unroll
-    for (int kb_ = 0; kb_ < NKB; ++kb_)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok = 16 * kb_ + 4 * grp + e < Sk;
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) S[kb_][i][e] = ok ? S[kb_][i][e] : -INFINITY;
+      for (int kb_ = 0; kb_ < NKB; ++kb_) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Ks[(16 * kb_ + col) * KP + 8 * grp]);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Ks[(16 * kb_ + col) * KP + 32 + 8 * grp]);
+        S[kb_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qc[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        S[kb_] = mfma_bf16(a1, Qc[1], S[kb_]);
       }
-  }
-  float l[NQB];
+      if (Sk < NK) {  // padded keys are set to -inf before the maximum is taken
 #pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    float mx = S[0][i][0];
+        for (int kb_ = 0; kb_ < NKB; ++kb_)
 #pragma unroll
-    for (int kb_ = 0; kb_ < NKB; ++kb_)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb_][i][e]);
-    const float mc = group4_max(mx) * c;
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb_ = 0; kb_ < NKB; ++kb_)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = fast_exp2(__builtin_fmaf(S[kb_][i][e], c, -mc));
-        S[kb_][i][e] = p;
-        ls += p;
+          for (int e = 0; e < 4; ++e) S[kb_][e] = 16 * kb_ + 4 * grp + e < Sk ? S[kb_][e] : -INFINITY;
       }
-    l[i] = group4_sum(ls);
-  }
-  f32x4 O[4][NQB];
+      float mx = S[0][0];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+      for (int kb_ = 0; kb_ < NKB; ++kb_)
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb_][e]);
+      const float mc = group4_max(mx) * c;
+      float ls = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < NKB / 2; ++ks) {
-    bf16x8 P[NQB];
+      for (int kb_ = 0; kb_ < NKB; ++kb_)
 #pragma unroll
-    for (int i = 0; i < NQB; ++i) P[i] = pack_bf16(S[2 * ks][i], S[2 * ks + 1][i]);
-    const int vrow = 32 * ks + 4 * grp + (col >> 2);
+        for (int e = 0; e < 4; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(S[kb_][e], c, -mc));
+          S[kb_][e] = p;
+          ls += p;
+        }
+      l = group4_sum(ls);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 a = cat_bf16(lds_read_tr16(&Vs[vrow * VP + vcol]), lds_read_tr16(&Vs[(vrow + 16) * VP + vcol]));
+      for (int ks = 0; ks < NKB / 2; ++ks) {
+        const bf16x8 P = pack_bf16(S[2 * ks], S[2 * ks + 1]);
+        const int vrow = 32 * ks + 4 * grp + (col >> 2);
 #pragma unroll
-      for (int i = 0; i < NQB; ++i) O[db][i] = mfma_bf16(a, P[i], O[db][i]);
+        for (int db = 0; db < 4; ++db) {
+          const int vcol = 16 * db + 4 * (col & 3);
+          const bf16x8 a =
+              cat_bf16(lds_read_tr16(&Vs[vrow * VP + vcol]), lds_read_tr16(&Vs[(vrow + 16) * VP + vcol]));
+          O[db] = mfma_bf16(a, P, O[db]);
+        }
+      }
+    } else {
+      float m = -INFINITY, lp = 0.0f;  // running maximum; this lane's share of the running sum
+      const int nch = (Sk + 63) >> 6;
+      for (int ch = 0; ch < nch; ++ch) {
+        f32x4 S[4];
+#pragma unroll
+        for (int kb_ = 0; kb_ < 4; ++kb_) {
+          const int r = 64 * ch + 16 * kb_ + col;
+          const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&Ks[r * KP + 8 * grp]);
+          const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&Ks[r * KP + 32 + 8 * grp]);
+          S[kb_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qc[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          S[kb_] = mfma_bf16(a1, Qc[1], S[kb_]);
+        }
+        if (64 * ch + 64 > Sk) {
+#pragma unroll
+          for (int kb_ = 0; kb_ < 4; ++kb_)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[kb_][e] = 64 * ch + 16 * kb_ + 4 * grp + e < Sk ? S[kb_][e] : -INFINITY;
+        }
+        float mx = S[0][0];
+#pragma unroll
+        for (int kb_ = 0; kb_ < 4; ++kb_)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb_][e]);
+        const float mnew = fmaxf(m, group4_max(mx));  // finite: chunk 0 holds key 0
+        const float alpha = fast_exp2((m - mnew) * c);  // 0 on the first chunk
+        const float mc = mnew * c;
+        float ls = 0.0f;
+#pragma unroll
+        for (int kb_ = 0; kb_ < 4; ++kb_)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = fast_exp2(__builtin_fmaf(S[kb_][e], c, -mc));
+            S[kb_][e] = p;
+            ls += p;
+          }
+        lp = __builtin_fmaf(lp, alpha, ls);
+        m = mnew;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) O[db] *= alpha;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 P = pack_bf16(S[2 * ks], S[2 * ks + 1]);
+          const int vrow = 64 * ch + 32 * ks + 4 * grp + (col >> 2);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int vcol = 16 * db + 4 * (col & 3);
+            const bf16x8 a =
+                cat_bf16(lds_read_tr16(&Vs[vrow * VP + vcol]), lds_read_tr16(&Vs[(vrow + 16) * VP + vcol]));
+            O[db] = mfma_bf16(a, P, O[db]);
+          }
+        }
+      }
+      l = group4_sum(lp);
     }
-  }
-  unsigned short* ob = o + bh * (size_t)Sq * HD;
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    const float inv = 1.0f / l[i];
-    const int row = q0 + 16 * i + col;
+    const float inv = 1.0f / l;
+    const int row = q0 + col;
     if (row < Sq) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(O[db][i][0] * inv, O[db][i][1] * inv, O[db][i][2] * inv, O[db][i][3] * inv));
+            pack4_bf16_bits(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv));
+    }
+    if constexpr (ONLINE) {
+      Qc[0] = Qn[0];
+      Qc[1] = Qn[1];
     }
   }
 }
@@ -867,23 +941,24 @@ __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __re
 // ---------------------------------------------------------------- launchers
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, int B, int H, int Sq, int Sk,
                            float scale, hipStream_t s) {
-  dim3 grid((Sq + F32_BQ - 1) / F32_BQ, B * H);
-  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(F32_BQ), 0, s, q, k, v, o, Sq, Sk, scale);
+  const int nqb = (Sq + F32_BQ - 1) / F32_BQ;
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(nqb * B * H), dim3(F32_BQ), 0, s, q, k, v, o, Sq, Sk, scale, nqb);
   return hipGetLastError();
 }
 
 namespace {
-// compute units of the current device (cached per device; 256 on MI355X)
+// compute units of the current device, cached per device (256 on MI355X).  Concurrent first
+// calls may both query the attribute; they store the same value, and the accesses are atomic.
 int cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
@@ -954,16 +1029,10 @@ static bool quad_plan(long long bh, int Sq, int cus, QuadPlan& p) {
   return ok;
 }
 
-hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
-                            unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
-  const float c = scale * LOG2E;
-  const long long bh = (long long)B * H;
-  const int cus = cu_count();
-  QuadPlan plan;
-  if (quad_plan(bh, Sq, cus, plan) && (long long)(plan.s0 + plan.s1) * cus < duo_cost(bh, Sq, cus)) {
-    hipLaunchKernelGGL(attn_bf16_quad, dim3(2 * cus), dim3(256), 0, s, q, k, v, o, Sq, Sk, c, plan);
-    return hipGetLastError();
-  }
+// Which bf16 head-dim-64 kernel (and layout) a call of this shape runs on `cus` CUs.
+enum DenseKind { DK_QUAD, DK_DUO33, DK_DUO32, DK_DUO22, DK_PIPE };
+static DenseKind choose_dense(long long bh, int Sq, int cus, QuadPlan& plan) {
+  if (quad_plan(bh, Sq, cus, plan) && (long long)(plan.s0 + plan.s1) * cus < duo_cost(bh, Sq, cus)) return DK_QUAD;
   if (bh * cdiv(Sq, 256) >= cus) {
     // one 8-wave block per CU: pick the query blocks per SIMD (NA + NB) that minimise
     // rounds x per-SIMD work, e.g. 3+3 (one round of 220 blocks) for B=2, H=10, S=4096
@@ -974,11 +1043,24 @@ hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, co
       const long long cost = cdiv(bh * cdiv(Sq, 64 * (na[i] + nb[i])), cus) * (na[i] + nb[i]);
       if (best_cost < 0 || cost < best_cost) { best = i; best_cost = cost; }
     }
-    if (best == 0) return duo_launch<3, 3>(q, k, v, o, B, H, Sq, Sk, c, s);
-    if (best == 1) return duo_launch<3, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
-    return duo_launch<2, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
+    return best == 0 ? DK_DUO33 : best == 1 ? DK_DUO32 : DK_DUO22;
   }
-  // small grids: 16 queries per wave, 4 waves per block, 4 waves per SIMD
+  return DK_PIPE;  // small grids: 16 queries per wave, 4 waves per block, 4 waves per SIMD
+}
+
+hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
+                            unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
+  const float c = scale * LOG2E;
+  QuadPlan plan;
+  switch (choose_dense((long long)B * H, Sq, cu_count(), plan)) {
+    case DK_QUAD:
+      hipLaunchKernelGGL(attn_bf16_quad, dim3(16 * plan.c8), dim3(256), 0, s, q, k, v, o, Sq, Sk, c, plan);
+      return hipGetLastError();
+    case DK_DUO33: return duo_launch<3, 3>(q, k, v, o, B, H, Sq, Sk, c, s);
+    case DK_DUO32: return duo_launch<3, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
+    case DK_DUO22: return duo_launch<2, 2>(q, k, v, o, B, H, Sq, Sk, c, s);
+    case DK_PIPE: break;
+  }
   constexpr int NQB = 1, NW = 4;
   const int nqb = (Sq + 16 * NQB * NW - 1) / (16 * NQB * NW);
   dim3 grid(nqb * B * H);  // one dimension: the kernel maps block -> (b, h, query block)
@@ -986,26 +1068,59 @@ hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, co
   return hipGetLastError();
 }
 
-template <int NKB, int NQB, int NW>
+const char* attn_bf16_kernel_name(int B, int H, int Sq) {
+  QuadPlan plan;
+  switch (choose_dense((long long)B * H, Sq, cu_count(), plan)) {
+    case DK_QUAD:
+      return plan.s0 == 3 ? (plan.s1 == 3 ? "attn_bf16_quad 3+3" : "attn_bf16_quad 3+2")
+                          : "attn_bf16_quad 2+2";
+    case DK_DUO33: return "attn_bf16_duo 3+3";
+    case DK_DUO32: return "attn_bf16_duo 3+2";
+    case DK_DUO22: return "attn_bf16_duo 2+2";
+    case DK_PIPE: break;
+  }
+  return "attn_bf16_pipe";
+}
+
+// Query chunks per (b, h).  Up to 128 keys a workgroup is small (<= 39 KB of LDS, four waves)
+// and several share a CU, so every wave takes one 16-query block: the most workgroups, whose
+// latencies overlap.  Larger key sets fill most of a CU's LDS (one workgroup per CU): then the
+// chunks are sized so that all workgroups fit one round on the chip.
+static void xattn_chunks(long long bh, int Sq, int nw, bool big, int cus, int& nchunk, int& qpc) {
+  const long long nblk = cdiv(Sq, 16);
+  long long n = big ? std::max(1LL, cus / bh) : cdiv(nblk, nw);  // not big: one block per wave
+  n = std::min(n, nblk);
+  qpc = (int)(16 * cdiv(nblk, n));
+  nchunk = (int)cdiv(Sq, qpc);
+}
+
+template <int NK, int NW, bool ONLINE>
 static hipError_t xlaunch(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                           unsigned short* o, int B, int H, int Sq, int Sk, float c, hipStream_t s) {
-  dim3 grid((Sq + 16 * NQB * NW - 1) / (16 * NQB * NW), B * H);
-  hipLaunchKernelGGL((xattn_bf16<NKB, NQB, NW>), grid, dim3(64 * NW), 0, s, q, k, v, o, Sq, Sk, c);
+  const long long bh = (long long)B * H;
+  int nchunk = 1, qpc = 16;
+  xattn_chunks(bh, Sq, NW, ONLINE && NK > 256, cu_count(), nchunk, qpc);
+  hipLaunchKernelGGL((xattn_bf16<NK, NW, ONLINE>), dim3((unsigned)(bh * nchunk)), dim3(64 * NW), 0, s, q, k, v, o,
+                     Sq, Sk, c, nchunk, qpc);
   return hipGetLastError();
 }
 
 hipError_t launch_xattn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                              unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s) {
   const float c = scale * LOG2E;
-  // one 16-query block per wave, four waves per block: the kernel is latency-bound, and more,
-  // thinner waves beat fewer with two query blocks each (6.8 vs 7.4 us for 77 keys, B=2, H=20,
-  // Sq=1024)
-  if (Sk <= 32) return xlaunch<2, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
-  if (Sk <= 64) return xlaunch<4, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
-  if (Sk <= 96) return xlaunch<6, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
-  if (Sk <= 128) return xlaunch<8, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
-  if (Sk <= 192) return xlaunch<12, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
-  return xlaunch<16, 1, 4>(q, k, v, o, B, H, Sq, Sk, c, s);
+  // up to 128 keys: every score of a query block in registers, one exact pass; longer key sets
+  // (up to the LDS budget, KA_XATTN_MAX_SK) in 64-key chunks out of LDS with an online softmax.
+  // Past 256 keys one workgroup fills most of a CU's LDS: sixteen waves, four per SIMD.
+  if (Sk <= 32) return xlaunch<32, 4, false>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 64) return xlaunch<64, 4, false>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 96) return xlaunch<96, 4, false>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 128) return xlaunch<128, 4, false>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 192) return xlaunch<192, 4, true>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 256) return xlaunch<256, 4, true>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 320) return xlaunch<320, 16, true>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 384) return xlaunch<384, 16, true>(q, k, v, o, B, H, Sq, Sk, c, s);
+  if (Sk <= 448) return xlaunch<448, 16, true>(q, k, v, o, B, H, Sq, Sk, c, s);
+  return xlaunch<512, 16, true>(q, k, v, o, B, H, Sq, Sk, c, s);
 }
 
 }  // namespace ka

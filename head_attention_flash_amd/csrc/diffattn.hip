@@ -309,7 +309,7 @@ __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsi
 
 template <int NKB, int WPE, int NORM>
 __global__ __launch_bounds__(64 * BAND_NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void diff_band(DiffArgs a, int nblk) {
+void diff_band(DiffArgs a, int nblk, int nstrip) {
   constexpr int HALO = 8 * NKB - 8;       // slab of query tile q0 starts at key q0 - HALO
   constexpr int NR = BAND_BM + 2 * HALO;  // ring rows
   __shared__ __align__(16) unsigned short K1s[NR * KPD];
@@ -320,10 +320,10 @@ void diff_band(DiffArgs a, int nblk) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4, cc = tid & 3;
   const int S = a.S, window = a.window;
-  const size_t bh = blockIdx.y;
+  const size_t bh = blockIdx.x / nstrip;  // one-dimensional grid: (b, h) major, strip minor
   const int h = (int)(bh % a.H);
   const size_t bb = bh / a.H;
-  const int strip0 = blockIdx.x * nblk * BAND_BM;
+  const int strip0 = (blockIdx.x % nstrip) * nblk * BAND_BM;
   const int pos0 = strip0 - HALO;  // position held by ring slot 0
   // one (b, h) slice of each tensor; rows outside [0, S) read as zero
   const bool has_keep = a.v_keep != nullptr;
@@ -536,7 +536,7 @@ __device__ __forceinline__ bool dpipe_softmax(f32x4 (&S)[4][NQB], int j0, int Sl
 // stages K1, K2 and V tiles (one 16-byte chunk of each per thread and tile).  At the end
 // branch-2 waves leave lambda O2 / l2 in LDS and branch-1 waves subtract it.
 template <bool BAND, int NORM>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void diff_flash_split(DiffArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void diff_flash_split(DiffArgs a, int nqb) {
   __shared__ __align__(16) unsigned short K1b[2][DBN * KPD];
   __shared__ __align__(16) unsigned short K2b[2][DBN * KPD];
   __shared__ __align__(16) unsigned short Vb[2][DBN * VPD];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int col = lane & 15, grp = lane >> 4;
   const int br = w >> 2;  // 0: branch 1, 1: branch 2 (wave-uniform)
   const int S = a.S, window = a.window;
-  const size_t bh = blockIdx.y;
+  const size_t bh = blockIdx.x / nqb;  // one-dimensional grid: (b, h) major, 64-query block minor
   const int h = (int)(bh % a.H);
   const size_t bb = bh / a.H;
   const size_t base = bh * (size_t)S * HD;  // of the workspace's contiguous planes
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   load_params<NORM>(sp, a);
   __syncthreads();
 
-  const int qblk0 = blockIdx.x * 64;
+  const int qblk0 = (blockIdx.x % nqb) * 64;
   const int q0 = qblk0 + 16 * (w & 3);
   const int p = q0 + col;
   f16x8 Qf[1][2];
@@ -734,18 +734,19 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
     const int nb = (a.S + BAND_BM - 1) / BAND_BM;
     int nblk = (int)(((long long)nb * BH + BAND_TARGET_WGS - 1) / BAND_TARGET_WGS);
     nblk = nblk < 1 ? 1 : (nblk > 16 ? 16 : nblk);
-    dim3 grid((nb + nblk - 1) / nblk, BH);
+    const int nstrip = (nb + nblk - 1) / nblk;
+    const dim3 grid(nstrip * BH);
     const bool narrow = a.window <= 24;
     if (a.norm == NORM_RMS) {
       if (narrow)
-        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk, nstrip);
       else
-        hipLaunchKernelGGL((diff_band<6, 2, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+        hipLaunchKernelGGL((diff_band<6, 2, NORM_RMS>), grid, dim3(64 * BAND_NW), 0, s, a, nblk, nstrip);
     } else {
       if (narrow)
-        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+        hipLaunchKernelGGL((diff_band<4, BAND_WPE, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk, nstrip);
       else
-        hipLaunchKernelGGL((diff_band<6, 2, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk);
+        hipLaunchKernelGGL((diff_band<6, 2, NORM_DYT>), grid, dim3(64 * BAND_NW), 0, s, a, nblk, nstrip);
     }
     return hipGetLastError();
   }
@@ -757,17 +758,18 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(diff_kprep<NORM_DYT>, kgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((a.S + 63) / 64, BH);
+  const int nqb = (a.S + 63) / 64;
+  const dim3 grid(nqb * BH);
   if (a.norm == NORM_RMS) {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash_split<true, NORM_RMS>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<true, NORM_RMS>), grid, dim3(512), 0, s, a, nqb);
     else
-      hipLaunchKernelGGL((diff_flash_split<false, NORM_RMS>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<false, NORM_RMS>), grid, dim3(512), 0, s, a, nqb);
   } else {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash_split<true, NORM_DYT>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<true, NORM_DYT>), grid, dim3(512), 0, s, a, nqb);
     else
-      hipLaunchKernelGGL((diff_flash_split<false, NORM_DYT>), grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL((diff_flash_split<false, NORM_DYT>), grid, dim3(512), 0, s, a, nqb);
   }
   return hipGetLastError();
 }

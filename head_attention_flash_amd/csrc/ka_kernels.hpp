@@ -11,6 +11,8 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            float scale, hipStream_t s);
 hipError_t launch_attn_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                             unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s);
+// name and layout of the kernel launch_attn_bf16 picks for this shape on the current device
+const char* attn_bf16_kernel_name(int B, int H, int Sq);
 // head dim 512 (one kernel, bf16): the SDXL VAE's single-head attention
 hipError_t launch_attn512_bf16(const unsigned short* q, const unsigned short* k, const unsigned short* v,
                                unsigned short* o, int B, int H, int Sq, int Sk, float scale, hipStream_t s);

@@ -112,6 +112,17 @@ def make_diff_params(H: int, seed: int, alpha: float = 0.5, gamma_lo: float = 2.
     return a, g, b, lm
 
 
+def make_diff_params_varied(H: int, seed: int):
+    """Parameters that tell the four sets and the heads apart: alpha ~ U[0.3, 0.9] per set, gamma ~
+    U[2, 8] and beta ~ N(0, 0.3) per set and channel, lambda ~ U[0.2, 0.9] per head (float32)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    a = r.uniform(0.3, 0.9, 4).astype(np.float32)
+    g = r.uniform(2.0, 8.0, (4, D)).astype(np.float32)
+    b = r.normal(0.0, 0.3, (4, D)).astype(np.float32)
+    lm = r.uniform(0.2, 0.9, H).astype(np.float32)
+    return a, g, b, lm
+
+
 def make_diff(wl: Workload, seed_base: int | None = None, S: int | None = None, B: int | None = None,
               H: int | None = None):
     """q1, k1, q2, k2, v [B,H,S,D] bf16 bits and (alpha, gamma, beta, lambda)."""

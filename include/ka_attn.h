@@ -23,8 +23,13 @@
  *     float32 accumulation; softmax, DyT, rotary embedding and the branch
  *     subtraction in float32).
  *   - Work is enqueued on `stream` and nothing else; the call returns without
- *     waiting.  Results are bitwise deterministic (no atomics).  The library has
- *     no mutable global state, so concurrent calls on different streams are safe.
+ *     waiting.  Results are bitwise deterministic (no atomics).  Concurrent calls
+ *     on different streams are safe: the library's only host state is a per-device
+ *     cache of the CU count (atomic) and per-thread caches (the last HIP error,
+ *     the last dense plan).
+ *   - Shapes: B, H, Sq, Sk >= 1 and B*H*ceil(Sq/64) < 2^23 (every launch is a
+ *     one-dimensional grid whose work-item count must fit 32 bits); otherwise
+ *     KA_ERR_SHAPE.
  *   - Arguments are validated on the host before any HIP call; on failure
  *     nothing is enqueued and a status code is returned.  A failed launch
  *     returns KA_ERR_HIP and ka_last_hip_error() holds the hipError_t (per
@@ -58,8 +63,9 @@ typedef enum {
 
 typedef enum { KA_F32 = 0, KA_BF16 = 1 } ka_dtype;
 
-/* Largest key count ka_xattn_fwd holds on chip (longer key sets stream through). */
-#define KA_XATTN_MAX_SK 256
+/* Largest key count ka_xattn_fwd holds on chip (longer key sets stream through): 512
+ * keys and values at 304 bytes per key fill 152 KB of a CU's 160 KB of LDS. */
+#define KA_XATTN_MAX_SK 512
 
 /*
  * Dense scaled-dot-product attention, no mask.
@@ -81,7 +87,9 @@ ka_status ka_attn_fwd(ka_dtype dtype, const void* q, const void* k, const void* 
  * inventory" s1.2 and s5.7; Stable Audio 3's 257 conditioning tokens, "401 ->
  * 163 ms..." appendix D2).  With 1 <= Sk <= KA_XATTN_MAX_SK all keys and values
  * of a (b, h) are held in LDS and re-read by every query tile, queries streaming
- * through; longer key sets stream through LDS in tiles (the ka_attn_fwd kernels).
+ * through (up to 128 keys one exact softmax pass, beyond that 64-key chunks with
+ * an online softmax); longer key sets stream through LDS in tiles (the
+ * ka_attn_fwd kernels).
  * Any Sk >= 1.
  *   dtype KA_BF16 (KA_F32 is accepted and routed to the fp32 kernel).
  */
@@ -164,6 +172,12 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
  * v_keep the first 2*B*H*S*64*2 bytes suffice).  Returns 0 for invalid shapes as
  * well; the call then reports the error. */
 size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window);
+
+/* Name of the kernel (and query layout) ka_attn_fwd launches for this shape on the
+ * current device, e.g. "attn_bf16_quad 3+2", "attn_bf16_duo 3+3", "attn_bf16_pipe",
+ * "attn_f32", "attn512_bf16"; NULL for a shape or dtype ka_attn_fwd rejects.  A static
+ * string.  For tuning and for checks that every layout computes the same result. */
+const char* ka_attn_kernel_name(ka_dtype dtype, int B, int H, int Sq, int Sk, int D);
 
 /* Static description of a status code. */
 const char* ka_status_string(ka_status status);

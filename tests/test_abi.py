@@ -194,3 +194,94 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError):
         ka.ka_attn_fwd(x, x, x, o=torch.zeros_like(x))
+
+
+def test_grid_limit_is_a_shape_error(lib):
+    # B*H*ceil(Sq/64) must stay below 2^23 (one-dimensional grids, 32-bit work-item counts)
+    assert dense(lib, "ka_attn_fwd", H=1 << 23, Sq=1, Sk=1) == _lib.KA_ERR_SHAPE
+    assert dense(lib, "ka_attn_fwd", H=1 << 22, Sq=65, Sk=1) == _lib.KA_ERR_SHAPE
+    assert dense(lib, "ka_attn_fwd", H=(1 << 23) - 1, Sq=64, Sk=1, o=Q) == _lib.KA_ERR_ALIAS  # accepted shape
+    assert dense(lib, "ka_xattn_fwd", B=2, H=1 << 22, Sq=1, Sk=77) == _lib.KA_ERR_SHAPE
+    assert diff(lib, B=1, H=1 << 23, Sq=1, Sk=1) == _lib.KA_ERR_SHAPE
+    assert diff_ex(lib, B=1, H=1 << 22, Sq=100, Sk=100) == _lib.KA_ERR_SHAPE
+    assert lib.ka_last_hip_error() == 0
+
+
+def test_parameter_arrays_may_not_overlap_outputs(lib):
+    # o over alpha, gamma, beta or lambda (DyT); over rms_weight (RMSNorm)
+    assert diff(lib, o=0x7000000, alpha=0x7000000 + 64) == _lib.KA_ERR_ALIAS
+    assert diff(lib, gamma=O + 512) == _lib.KA_ERR_ALIAS
+    assert diff(lib, beta=O + 16) == _lib.KA_ERR_ALIAS
+    assert diff(lib, lam=O + 1024) == _lib.KA_ERR_ALIAS
+    assert diff_ex(lib, rms_w=O + 32) == _lib.KA_ERR_ALIAS
+    # ... and the workspace over any of them (the full path)
+    need = 2 * 1 * 2 * 8 * 64 * 2  # the prepared keys: all a call without V flags uses
+    assert diff(lib, window=-1, ws=G - 64, ws_bytes=need) == _lib.KA_ERR_ALIAS
+    assert diff(lib, window=-1, ws=L - need + 16, ws_bytes=need) == _lib.KA_ERR_ALIAS
+    assert diff_ex(lib, window=-1, ws=G - 16, ws_bytes=3 * need // 2) == _lib.KA_ERR_ALIAS
+    assert lib.ka_last_hip_error() == 0
+
+
+def test_kernel_name_introspection(lib):
+    # no GPU here: the launch plan assumes 256 CUs, MI355X's count
+    name = lambda *a: lib.ka_attn_kernel_name(*a)  # noqa: E731
+    assert name(ka.KA_BF16, 2, 10, 4096, 4096, 64).startswith(b"attn_bf16_quad")
+    assert name(ka.KA_BF16, 1, 1, 100, 100, 64) == b"attn_bf16_pipe"
+    assert name(ka.KA_BF16, 1, 256, 370, 333, 64) == b"attn_bf16_duo 3+3"
+    assert name(ka.KA_F32, 1, 2, 256, 256, 64) == b"attn_f32"
+    assert name(ka.KA_BF16, 1, 1, 16384, 16384, 512) == b"attn512_bf16"
+    assert name(ka.KA_F32, 1, 1, 16, 16, 512) is None
+    assert name(ka.KA_BF16, 0, 1, 16, 16, 64) is None
+    assert name(ka.KA_BF16, 1, 1 << 23, 1, 1, 64) is None
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_checks_shapes_dtypes_before_any_call(lib):
+    import torch
+    q, k, v = _cpu(1, 2, 8, 64), _cpu(1, 2, 5, 64), _cpu(1, 2, 5, 64)
+    bad = [dict(k=_cpu(1, 1, 5, 64)), dict(v=_cpu(1, 2, 6, 64)), dict(k=_cpu(1, 2, 5, 64, dtype=torch.float32)),
+           dict(o=_cpu(1, 2, 7, 64)), dict(o=_cpu(1, 2, 8, 64, dtype=torch.float32)), dict(q=_cpu(2, 8, 64))]
+    for fn in (ka.ka_attn_fwd, ka.ka_xattn_fwd):
+        for over in bad:
+            args = dict(q=q, k=k, v=v, o=None)
+            args.update(over)
+            with pytest.raises(ValueError):
+                fn(args["q"], args["k"], args["v"], o=args["o"])
+    with pytest.raises(TypeError):  # dtype the library does not take
+        ka.ka_attn_fwd(_cpu(1, 1, 4, 64, dtype=torch.float16), _cpu(1, 1, 4, 64, dtype=torch.float16),
+                       _cpu(1, 1, 4, 64, dtype=torch.float16))
+
+
+def test_binding_checks_differential_arguments(lib):
+    import torch
+    f32 = torch.float32
+    x = [_cpu(2, 3, 10, 64) for _ in range(5)]
+    a, g, b, lm = _cpu(4, dtype=f32), _cpu(4, 64, dtype=f32), _cpu(4, 64, dtype=f32), _cpu(3, dtype=f32)
+    good = dict(alpha=a, gamma=g, beta=b)
+    cases = [(dict(x=[x[0], _cpu(2, 3, 9, 64)] + x[2:]), good, lm),   # k1 rows
+             (dict(x=x[:4] + [_cpu(2, 2, 10, 64)]), good, lm),         # v heads
+             (dict(x=x), dict(good, gamma=_cpu(4, 32, dtype=f32)), lm),
+             (dict(x=x), dict(good, alpha=_cpu(4)), lm),               # bf16 alpha
+             (dict(x=x), good, _cpu(2, dtype=f32))]                    # lambda per head
+    for c, prm, lam in cases:
+        with pytest.raises(ValueError):
+            ka.ka_diffattn_fwd(*c["x"], prm["alpha"], prm["gamma"], prm["beta"], lam)
+    with pytest.raises(ValueError):  # o of the wrong shape
+        ka.ka_diffattn_fwd(*x, a, g, b, lm, o=_cpu(2, 3, 10, 32))
+    with pytest.raises(ValueError):  # V flags [B, S] uint8
+        ka.ka_diffattn_fwd_ex(*x, lm, qk_norm="rms", rms_weight=g, v_keep=_cpu(2, 11, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        ka.ka_diffattn_fwd_ex(*x, lm, qk_norm="rms", rms_weight=g, v_keep=_cpu(2, 10, dtype=torch.int32))
+    with pytest.raises(ValueError):  # RMSNorm needs its weights
+        ka.ka_diffattn_fwd_ex(*x, lm, qk_norm="rms")
+    with pytest.raises(ValueError):
+        ka.ka_diffattn_fwd_ex(*x, lm, qk_norm="layer")
+    with pytest.raises(ValueError):  # a workspace must be bytes
+        ka.ka_diffattn_fwd(*x, a, g, b, lm, workspace=_cpu(100, dtype=f32))
+    # well-formed CPU tensors pass every shape check and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        ka.ka_diffattn_fwd(*x, a, g, b, lm, window=17)
