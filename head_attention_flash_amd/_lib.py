@@ -21,8 +21,9 @@ KA_QKNORM_DYT, KA_QKNORM_RMS = 0, 1
 KA_XATTN_MAX_SK = 512
 
 # every symbol include/ka_attn.h declares
-EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_fwd_ex", "ka_diffattn_workspace_bytes",
-           "ka_attn_kernel_name", "ka_status_string", "ka_last_hip_error", "ka_version")
+EXPORTS = ("ka_attn_fwd", "ka_xattn_fwd", "ka_diffattn_fwd", "ka_diffattn_fwd_ex", "ka_diffattn_fwd_noalloc",
+           "ka_diffattn_workspace_bytes", "ka_attn_kernel_name", "ka_status_string", "ka_last_hip_error", "ka_version")
+KA_STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 class KaError(RuntimeError):
@@ -55,6 +56,9 @@ def load(path: str = LIB_PATH):
     lib.ka_diffattn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, vp, vp, f, i, f, vp,
                                        vp, vp, vp, sz, vp]
     lib.ka_diffattn_fwd_ex.restype = i
+    lib.ka_diffattn_fwd_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, vp, vp, vp, f, i, f,
+                                            vp, vp, vp, vp]
+    lib.ka_diffattn_fwd_noalloc.restype = i
     lib.ka_diffattn_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.ka_diffattn_workspace_bytes.restype = sz
     lib.ka_attn_kernel_name.argtypes = [i, i, i, i, i, i]
@@ -270,4 +274,36 @@ def ka_diffattn_fwd_ex(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, win
                                 ctypes.cast(layouts, ctypes.c_void_p) if layouts is not None else None, ws_ptr,
                                 ws_bytes, _stream(stream))
     _check(lib, st, "ka_diffattn_fwd_ex")
+    return o
+
+
+def ka_diffattn_fwd_noalloc(q1, k1, q2, k2, v, lam, o=None, scale: float = 0.125, window: int = -1,
+                            qk_norm: str = "dyt", alpha=None, gamma=None, beta=None, rms_weight=None,
+                            rms_eps: float = 1e-6, rotary_dims: int = 64, rope_base: float = 10000.0, v_keep=None,
+                            stream=None):
+    """ka_diffattn_fwd_ex without a workspace: the library's per-GPU scratch array (KA_STATIC_WORKSPACE_BYTES)
+    serves the full path, and the call allocates nothing (pass o to avoid torch allocating the output).
+    Calls that overlap in time on one GPU share that array and race."""
+    lib = load()
+    if qk_norm not in ("dyt", "rms"):
+        raise ValueError(f"qk_norm must be 'dyt' or 'rms', got {qk_norm!r}")
+    prm = ((("alpha", alpha, (4,)), ("gamma", gamma, (4, 64)), ("beta", beta, (4, 64))) if qk_norm == "dyt"
+           else (("rms_weight", rms_weight, (4, 64)),))
+    _check_diff(q1, k1, q2, k2, v, o, lam, prm, v_keep=v_keep)
+    B, H, S, D = q1.shape
+    if o is None:
+        o = _torch().empty_like(q1)
+    norm = {"dyt": KA_QKNORM_DYT, "rms": KA_QKNORM_RMS}[qk_norm]
+    opt = lambda t, name: _dev(t, name) if t is not None else ctypes.c_void_p(0)  # noqa: E731
+    views = [_dev_view(t, n) for t, n in ((q1, "q1"), (k1, "k1"), (q2, "q2"), (k2, "k2"), (v, "v"), (o, "o"))]
+    layouts = None
+    if not all(t.is_contiguous() for t in (q1, k1, q2, k2, v, o)):
+        layouts = (KaLayout * 6)(*[lay for _, lay in views])
+    st = lib.ka_diffattn_fwd_noalloc(_dtype_code(q1), *[ptr for ptr, _ in views], B, H, S, S, D, float(scale),
+                                     int(window), norm, opt(alpha, "alpha"), opt(gamma, "gamma"), opt(beta, "beta"),
+                                     opt(rms_weight, "rms_weight"), float(rms_eps), int(rotary_dims),
+                                     float(rope_base), _dev(lam, "lambda"), opt(v_keep, "v_keep"),
+                                     ctypes.cast(layouts, ctypes.c_void_p) if layouts is not None else None,
+                                     _stream(stream))
+    _check(lib, st, "ka_diffattn_fwd_noalloc")
     return o

@@ -98,6 +98,122 @@ bool view_injective(const ka_layout& L, int B, int H, int S) {
   return true;
 }
 
+// Validates a differential call and fills *out.  dry: stop after the shape, parameter,
+// layout and output checks and report the workspace bytes the call needs in *need (no
+// workspace checks, *out untouched).
+ka_status diff_build(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                            const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
+                            ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma, const float* dyt_beta,
+                            const float* rms_weight, float rms_eps, int rotary_dims, float rope_base,
+                            const float* lambda, const uint8_t* v_keep, const ka_layout* layouts, void* workspace,
+                            size_t workspace_bytes, bool dry, size_t* need_out, ka::DiffArgs* out) {
+  if (qk_norm != KA_QKNORM_DYT && qk_norm != KA_QKNORM_RMS) return KA_ERR_UNSUPPORTED;
+  if (!q1 || !k1 || !q2 || !k2 || !v || !o || !lambda) return KA_ERR_NULL;
+  if (qk_norm == KA_QKNORM_DYT && (!dyt_alpha || !dyt_gamma || !dyt_beta)) return KA_ERR_NULL;
+  if (qk_norm == KA_QKNORM_RMS && !rms_weight) return KA_ERR_NULL;
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || Sq != Sk) return KA_ERR_SHAPE;
+  if (D != 64 || dtype != KA_BF16) return KA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(rope_base) || !(rope_base > 1.0f))
+    return KA_ERR_PARAM;
+  if (rotary_dims != 32 && rotary_dims != 64) return KA_ERR_PARAM;
+  if (qk_norm == KA_QKNORM_RMS && (!std::isfinite(rms_eps) || !(rms_eps > 0.0f))) return KA_ERR_PARAM;
+  const int S = Sq;
+  size_t tb = 0;
+  if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
+  if (!grid_ok(B, H, S)) return KA_ERR_SHAPE;
+  // views of q1, k1, q2, k2, v, o: the given strides, or contiguous [B][H][S][64]
+  ka_layout lay[6];
+  size_t ext[6];
+  for (int t = 0; t < 6; ++t) {
+    lay[t] = layouts ? layouts[t] : ka_layout{(int64_t)H * S * 64, (int64_t)S * 64, 64};
+    if (!view_ok(lay[t], B, H, S, &ext[t])) return KA_ERR_SHAPE;
+  }
+  if (!view_injective(lay[5], B, H, S)) return KA_ERR_SHAPE;  // rows of o written twice
+  const void* ins[5] = {q1, k1, q2, k2, v};
+  for (const void* p : ins)
+    if (!aligned16(p)) return KA_ERR_ALIGN;
+  if (!aligned16(o)) return KA_ERR_ALIGN;
+  const size_t need = ka::diff_workspace_bytes(B, H, S, window, v_keep != nullptr);
+  *need_out = need;
+  // o against the extents [base, base + ext) of the input views (inputs may share memory with
+  // each other), the V flags and the parameter arrays, which every workgroup reads while others
+  // write o
+  const void* prm[5] = {dyt_alpha, dyt_gamma, dyt_beta, rms_weight, lambda};
+  const size_t prm_bytes[5] = {4 * sizeof(float), 4 * HD_ * sizeof(float), 4 * HD_ * sizeof(float),
+                               4 * HD_ * sizeof(float), (size_t)H * sizeof(float)};
+  const bool prm_used[5] = {qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT,
+                            qk_norm == KA_QKNORM_RMS, true};
+  const size_t nk = v_keep ? (size_t)B * S : 0;
+  for (int t = 0; t < 5; ++t)
+    if (overlap(o, ext[5], ins[t], ext[t])) return KA_ERR_ALIAS;
+  if (overlap(o, ext[5], v_keep, nk)) return KA_ERR_ALIAS;
+  for (int t = 0; t < 5; ++t)
+    if (prm_used[t] && overlap(o, ext[5], prm[t], prm_bytes[t])) return KA_ERR_ALIAS;
+  if (dry) return KA_OK;
+  if (need) {
+    if (!workspace) return KA_ERR_NULL;
+    if (workspace_bytes < need) return KA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KA_ERR_ALIGN;
+    // the workspace against o, the inputs, the V flags and the parameter arrays
+    if (overlap(o, ext[5], workspace, need)) return KA_ERR_ALIAS;
+    for (int t = 0; t < 5; ++t)
+      if (overlap(workspace, need, ins[t], ext[t])) return KA_ERR_ALIAS;
+    if (overlap(workspace, need, v_keep, nk)) return KA_ERR_ALIAS;
+    for (int t = 0; t < 5; ++t)
+      if (prm_used[t] && overlap(workspace, need, prm[t], prm_bytes[t])) return KA_ERR_ALIAS;
+  }
+
+  ka::DiffArgs& a = *out;
+  std::memset(&a, 0, sizeof(a));
+  a.q1 = static_cast<const unsigned short*>(q1);
+  a.k1 = static_cast<const unsigned short*>(k1);
+  a.q2 = static_cast<const unsigned short*>(q2);
+  a.k2 = static_cast<const unsigned short*>(k2);
+  a.v = static_cast<const unsigned short*>(v);
+  a.o = static_cast<unsigned short*>(o);
+  a.ws = static_cast<_Float16*>(workspace);
+  a.alpha = dyt_alpha;
+  a.gamma = dyt_gamma;
+  a.beta = dyt_beta;
+  a.rms_w = rms_weight;
+  a.lambda = lambda;
+  a.v_keep = v_keep;
+  a.norm = qk_norm == KA_QKNORM_RMS ? 1 : 0;
+  a.rms_eps = rms_eps;
+  a.rot32 = rotary_dims == 32;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  for (int t = 0; t < 6; ++t) {
+    a.sb[t] = lay[t].batch;
+    a.sh[t] = lay[t].head;
+    a.st[t] = (int)lay[t].token;
+  }
+  a.window = window < 0 ? -1 : window;
+  a.c = scale * 1.4426950408889634f;
+  const double two_pi = 6.283185307179586476925286766559;
+  // positions need ceil(log2 S) bits; rev_hi keeps 24 - that many significant bits so
+  // that p * rev_hi is exact in fp32, and rev_lo carries the rest
+  int pbits = 1;
+  while ((1 << pbits) < S) ++pbits;
+  a.split_angles = pbits <= 16;
+  // pair i: 64 rotary dims pair (i, i+32) for i < 32; 32 rotary dims pair (i, i+16) for
+  // i < 16 at base^(-2i/32), and the threads' pairs 16..31 hold unrotated dims (angle 0)
+  for (int i = 0; i < 32; ++i) {
+    const double r = rotary_dims == 64 ? std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi
+                     : i < 16         ? std::pow((double)rope_base, -2.0 * i / 32.0) / two_pi
+                                      : 0.0;
+    a.rev[i] = r;
+    int ex = 0;
+    std::frexp(r, &ex);                                // r = m * 2^ex, 0.5 <= m < 1 (r = 0: 0)
+    const double q = std::ldexp(1.0, ex - (24 - pbits));
+    const double hi = std::round(r / q) * q;           // 24 - pbits significant bits
+    a.rev_hi[i] = (float)hi;
+    a.rev_lo[i] = (float)(r - hi);
+  }
+  return KA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,112 +267,38 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
                              const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
                              float rope_base, const float* lambda, const uint8_t* v_keep, const ka_layout* layouts,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (qk_norm != KA_QKNORM_DYT && qk_norm != KA_QKNORM_RMS) return KA_ERR_UNSUPPORTED;
-  if (!q1 || !k1 || !q2 || !k2 || !v || !o || !lambda) return KA_ERR_NULL;
-  if (qk_norm == KA_QKNORM_DYT && (!dyt_alpha || !dyt_gamma || !dyt_beta)) return KA_ERR_NULL;
-  if (qk_norm == KA_QKNORM_RMS && !rms_weight) return KA_ERR_NULL;
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1 || Sq != Sk) return KA_ERR_SHAPE;
-  if (D != 64 || dtype != KA_BF16) return KA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.0f) || !std::isfinite(rope_base) || !(rope_base > 1.0f))
-    return KA_ERR_PARAM;
-  if (rotary_dims != 32 && rotary_dims != 64) return KA_ERR_PARAM;
-  if (qk_norm == KA_QKNORM_RMS && (!std::isfinite(rms_eps) || !(rms_eps > 0.0f))) return KA_ERR_PARAM;
-  const int S = Sq;
-  size_t tb = 0;
-  if (!tensor_bytes(B, H, S, D, 2, &tb)) return KA_ERR_SHAPE;
-  if (!grid_ok(B, H, S)) return KA_ERR_SHAPE;
-  // views of q1, k1, q2, k2, v, o: the given strides, or contiguous [B][H][S][64]
-  ka_layout lay[6];
-  size_t ext[6];
-  for (int t = 0; t < 6; ++t) {
-    lay[t] = layouts ? layouts[t] : ka_layout{(int64_t)H * S * 64, (int64_t)S * 64, 64};
-    if (!view_ok(lay[t], B, H, S, &ext[t])) return KA_ERR_SHAPE;
-  }
-  if (!view_injective(lay[5], B, H, S)) return KA_ERR_SHAPE;  // rows of o written twice
-  const void* ins[5] = {q1, k1, q2, k2, v};
-  for (const void* p : ins)
-    if (!aligned16(p)) return KA_ERR_ALIGN;
-  if (!aligned16(o)) return KA_ERR_ALIGN;
-  const size_t need = ka::diff_workspace_bytes(B, H, S, window, v_keep != nullptr);
-  if (need) {
-    if (!workspace) return KA_ERR_NULL;
-    if (workspace_bytes < need) return KA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return KA_ERR_ALIGN;
-  }
-  // the extents [base, base + ext) of the views; inputs may share memory with each other
-  for (int t = 0; t < 5; ++t)
-    if (overlap(o, ext[5], ins[t], ext[t])) return KA_ERR_ALIAS;
-  if (need && overlap(o, ext[5], workspace, need)) return KA_ERR_ALIAS;
-  if (need)
-    for (int t = 0; t < 5; ++t)
-      if (overlap(workspace, need, ins[t], ext[t])) return KA_ERR_ALIAS;
-  if (v_keep) {
-    const size_t nk = (size_t)B * S;
-    if (overlap(o, ext[5], v_keep, nk) || (need && overlap(workspace, need, v_keep, nk))) return KA_ERR_ALIAS;
-  }
-  // the parameter arrays are read by every workgroup while others write o and the workspace
-  const void* prm[4] = {dyt_alpha, dyt_gamma, dyt_beta, rms_weight};
-  const size_t prm_bytes[4] = {4 * sizeof(float), 4 * HD_ * sizeof(float), 4 * HD_ * sizeof(float),
-                               4 * HD_ * sizeof(float)};
-  const bool prm_used[4] = {qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT, qk_norm == KA_QKNORM_DYT,
-                            qk_norm == KA_QKNORM_RMS};
-  for (int t = 0; t < 4; ++t) {
-    if (!prm_used[t]) continue;
-    if (overlap(o, ext[5], prm[t], prm_bytes[t]) || (need && overlap(workspace, need, prm[t], prm_bytes[t])))
-      return KA_ERR_ALIAS;
-  }
-  if (overlap(o, ext[5], lambda, (size_t)H * sizeof(float)) ||
-      (need && overlap(workspace, need, lambda, (size_t)H * sizeof(float))))
-    return KA_ERR_ALIAS;
-
   ka::DiffArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.q1 = static_cast<const unsigned short*>(q1);
-  a.k1 = static_cast<const unsigned short*>(k1);
-  a.q2 = static_cast<const unsigned short*>(q2);
-  a.k2 = static_cast<const unsigned short*>(k2);
-  a.v = static_cast<const unsigned short*>(v);
-  a.o = static_cast<unsigned short*>(o);
-  a.ws = static_cast<_Float16*>(workspace);
-  a.alpha = dyt_alpha;
-  a.gamma = dyt_gamma;
-  a.beta = dyt_beta;
-  a.rms_w = rms_weight;
-  a.lambda = lambda;
-  a.v_keep = v_keep;
-  a.norm = qk_norm == KA_QKNORM_RMS ? 1 : 0;
-  a.rms_eps = rms_eps;
-  a.rot32 = rotary_dims == 32;
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  for (int t = 0; t < 6; ++t) {
-    a.sb[t] = lay[t].batch;
-    a.sh[t] = lay[t].head;
-    a.st[t] = (int)lay[t].token;
+  size_t need = 0;
+  const ka_status st = diff_build(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, qk_norm, dyt_alpha,
+                                  dyt_gamma, dyt_beta, rms_weight, rms_eps, rotary_dims, rope_base, lambda, v_keep,
+                                  layouts, workspace, workspace_bytes, false, &need, &a);
+  if (st != KA_OK) return st;
+  return hip_status(ka::launch_diffattn(a, stream));
+}
+
+ka_status ka_diffattn_fwd_noalloc(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                                  const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale,
+                                  int window, ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
+                                  const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
+                                  float rope_base, const float* lambda, const uint8_t* v_keep,
+                                  const ka_layout* layouts, hipStream_t stream) {
+  size_t need = 0;
+  ka_status st = diff_build(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, qk_norm, dyt_alpha,
+                            dyt_gamma, dyt_beta, rms_weight, rms_eps, rotary_dims, rope_base, lambda, v_keep, layouts,
+                            nullptr, 0, true, &need, nullptr);
+  if (st != KA_OK) return st;
+  if (need > KA_STATIC_WORKSPACE_BYTES) return KA_ERR_WORKSPACE;  // before any HIP call
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (need) {
+    const hipError_t e = ka::diff_static_workspace(&ws, &ws_bytes);
+    if (e != hipSuccess) return hip_status(e);
   }
-  a.window = window < 0 ? -1 : window;
-  a.c = scale * 1.4426950408889634f;
-  const double two_pi = 6.283185307179586476925286766559;
-  // positions need ceil(log2 S) bits; rev_hi keeps 24 - that many significant bits so
-  // that p * rev_hi is exact in fp32, and rev_lo carries the rest
-  int pbits = 1;
-  while ((1 << pbits) < S) ++pbits;
-  a.split_angles = pbits <= 16;
-  // pair i: 64 rotary dims pair (i, i+32) for i < 32; 32 rotary dims pair (i, i+16) for
-  // i < 16 at base^(-2i/32), and the threads' pairs 16..31 hold unrotated dims (angle 0)
-  for (int i = 0; i < 32; ++i) {
-    const double r = rotary_dims == 64 ? std::pow((double)rope_base, -2.0 * i / 64.0) / two_pi
-                     : i < 16         ? std::pow((double)rope_base, -2.0 * i / 32.0) / two_pi
-                                      : 0.0;
-    a.rev[i] = r;
-    int ex = 0;
-    std::frexp(r, &ex);                                // r = m * 2^ex, 0.5 <= m < 1 (r = 0: 0)
-    const double q = std::ldexp(1.0, ex - (24 - pbits));
-    const double hi = std::round(r / q) * q;           // 24 - pbits significant bits
-    a.rev_hi[i] = (float)hi;
-    a.rev_lo[i] = (float)(r - hi);
-  }
+  ka::DiffArgs a;
+  st = diff_build(dtype, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, scale, window, qk_norm, dyt_alpha, dyt_gamma,
+                  dyt_beta, rms_weight, rms_eps, rotary_dims, rope_base, lambda, v_keep, layouts, ws, ws_bytes, false,
+                  &need, &a);
+  if (st != KA_OK) return st;
   return hip_status(ka::launch_diffattn(a, stream));
 }
 

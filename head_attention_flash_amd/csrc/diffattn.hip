@@ -42,8 +42,10 @@
 //   diff_flash_split   pass 2: eight waves per 64 queries, one branch per wave; q prep
 //                      in registers, then a pipelined flash loop over 64-key tiles of the
 //                      prepared keys and V; branch 2 is subtracted through LDS at the end.
+#include <mutex>
 #include <type_traits>
 
+#include "ka_attn.h"
 #include "ka_common.hpp"
 #include "ka_kernels.hpp"
 
@@ -723,6 +725,35 @@ static bool use_band(int S, int window) { return window >= 0 && window < S - 1 &
 size_t diff_workspace_bytes(int B, int H, int S, int window, bool v_flags) {
   if (use_band(S, window)) return 0;
   return (size_t)(v_flags ? 3 : 2) * B * H * S * HD * sizeof(_Float16);
+}
+
+// ---------------------------------------------------------------- allocation-free workspace
+// One copy per GPU of a file-scope device array, for callers that cannot allocate (stream
+// capture, serving loops).  On the host the array's name only stands in for the symbol: its
+// device address comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever passed to a kernel.  The array keeps the last
+// call's contents; the full path overwrites every byte it reads (prepared keys) before
+// reading it, so nothing is cleared.  Calls that overlap on one GPU share it and race.
+__device__ __align__(256) unsigned char scratch[KA_STATIC_WORKSPACE_BYTES];
+
+hipError_t diff_static_workspace(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = KA_STATIC_WORKSPACE_BYTES;
+  return hipSuccess;
 }
 
 hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {

@@ -55,6 +55,9 @@ struct DiffArgs {
 constexpr int BAND_MAX_WINDOW = 40;
 
 size_t diff_workspace_bytes(int B, int H, int S, int window, bool v_flags);
+// The allocation-free workspace of ka_diffattn_fwd_noalloc: this device's copy of a file-scope
+// device array of KA_STATIC_WORKSPACE_BYTES; its address is looked up once per device.
+hipError_t diff_static_workspace(void** ptr, size_t* bytes);
 hipError_t launch_diffattn(const DiffArgs& a, hipStream_t s);
 
 }  // namespace ka

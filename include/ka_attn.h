@@ -166,6 +166,30 @@ ka_status ka_diffattn_fwd_ex(ka_dtype dtype, const void* q1, const void* k1, con
                              const ka_layout* layouts, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Size of the device scratch array behind ka_diffattn_fwd_noalloc (one copy per GPU). */
+#define KA_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/*
+ * ka_diffattn_fwd_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  The full path's scratch (ka_diffattn_workspace_bytes of the shape) comes
+ * from a file-scope device array of KA_STATIC_WORKSPACE_BYTES that each GPU holds for the
+ * life of the process; the call itself allocates and frees nothing.  Shapes needing more
+ * return KA_ERR_WORKSPACE (before any HIP call): 32 MiB covers B*H*S up to 87,381 rows
+ * (the 1422-token DiT shape with 16 heads needs 8.7 MB).  Calls on one GPU share the array:
+ * calls that overlap in time on one GPU (different streams, or different threads without
+ * ordering) race on it and give undefined results; calls ordered on one stream are safe.
+ * The banded path needs no scratch.  Everything else is as for ka_diffattn_fwd_ex; the
+ * first call on a device looks up the array's address (a HIP call; a failure returns
+ * KA_ERR_HIP).
+ */
+ka_status ka_diffattn_fwd_noalloc(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                                  const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale,
+                                  int window, ka_qknorm qk_norm, const float* dyt_alpha, const float* dyt_gamma,
+                                  const float* dyt_beta, const float* rms_weight, float rms_eps, int rotary_dims,
+                                  float rope_base, const float* lambda, const uint8_t* v_keep,
+                                  const ka_layout* layouts, hipStream_t stream);
+
 /* Workspace bytes ka_diffattn_fwd and ka_diffattn_fwd_ex need for this shape: 0 for
  * the banded path; for the full path the prepared keys (2*B*H*S*64 fp16) plus room
  * for a flagged copy of V (B*H*S*64 bf16), which only calls with v_keep use (without

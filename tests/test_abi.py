@@ -285,3 +285,28 @@ def test_binding_checks_differential_arguments(lib):
     # well-formed CPU tensors pass every shape check and stop at the device check
     with pytest.raises(ValueError, match="GPU"):
         ka.ka_diffattn_fwd(*x, a, g, b, lm, window=17)
+
+
+def diff_na(lib, dt=ka.KA_BF16, q1=Q, k1=K, q2=V, k2=O2, v=A, o=O, B=1, H=2, Sq=8, Sk=8, D=64, scale=0.125,
+            window=-1, norm=ka.KA_QKNORM_RMS, alpha=0, gamma=0, beta=0, rms_w=G, eps=1e-6, rot=32, base=10000.0,
+            lam=L, keep=KEEP, layouts=None):
+    return lib.ka_diffattn_fwd_noalloc(dt, q1, k1, q2, k2, v, o, B, H, Sq, Sk, D, ctypes.c_float(scale), window,
+                                       norm, alpha, gamma, beta, rms_w, ctypes.c_float(eps), rot,
+                                       ctypes.c_float(base), lam, keep, layouts, None)
+
+
+def test_noalloc_validation(lib):
+    # the same argument checks as ka_diffattn_fwd_ex, all before any HIP call
+    assert diff_na(lib, norm=7) == _lib.KA_ERR_UNSUPPORTED
+    assert diff_na(lib, rms_w=0) == _lib.KA_ERR_NULL
+    assert diff_na(lib, q2=0) == _lib.KA_ERR_NULL
+    assert diff_na(lib, Sk=9) == _lib.KA_ERR_SHAPE
+    assert diff_na(lib, rot=48) == _lib.KA_ERR_PARAM
+    assert diff_na(lib, o=Q) == _lib.KA_ERR_ALIAS
+    assert diff_na(lib, v=A + 4) == _lib.KA_ERR_ALIGN
+    # a shape whose full-path scratch exceeds the static array is refused before any HIP call
+    rows = _lib.KA_STATIC_WORKSPACE_BYTES // (3 * 64 * 2) + 1
+    big = dict(q1=0x10000000, k1=0x20000000, q2=0x30000000, k2=0x40000000, v=0x50000000, o=0x60000000,
+               keep=0x70000000)
+    assert diff_na(lib, B=1, H=1, Sq=rows, Sk=rows, **big) == _lib.KA_ERR_WORKSPACE
+    assert lib.ka_last_hip_error() == 0
