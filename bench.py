@@ -7,9 +7,11 @@ other forms of the hot path -- cross-attention against 77 keys, banded and full
 differential attention -- are timed the same way and reported under "forms",
 each against its own roofline (MFMA for the dense forms, HBM for the banded one).
 Kernel time is measured with HIP events recorded on the stream the kernels run
-on.  HBM-bound forms rotate several input copies so that the 256 MB last-level
-cache does not serve them.  The fp64 CPU oracle is timed on a bounded sample of
-the same workload for `cpu_baseline`.
+on.  Every form is timed over rotated input copies (together past the 256 MB
+last-level cache, so inputs come from HBM: "us", the reported figure) and hot
+(one copy again and again: "us_hot").  The fp64 CPU oracle is timed on the same
+dense workload for `cpu_baseline`.  `--trace-summary` turns a rocprofv3 kernel
+trace of this command into per-kernel median, mean, min and max durations.
 """
 from __future__ import annotations
 
@@ -70,6 +72,14 @@ def time_launches(fn, nsets, steps, warmup, torch):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def time_graph_hot_and_rotated(fn, nsets, steps, warmup, torch):
+    """(rotated, hot): seconds per launch over `nsets` rotated input copies (past the last-level cache),
+    and over one copy launched again and again (served largely from the caches)."""
+    rot = time_graph(fn, nsets, steps, warmup, torch)
+    hot = time_graph(fn, 1, steps, warmup, torch) if nsets > 1 else rot
+    return rot, hot
 
 
 def time_graph(fn, nsets, steps, warmup, torch):
@@ -151,11 +161,33 @@ def cpu_baseline(wl):
             "sample": f"the whole {wl.key} workload ({wl.B * wl.H * wl.Sq} query rows x {wl.Sk} keys), {dt:.2f} s"}
 
 
+def host_cpu():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gcc_version():
+    import subprocess
+    try:
+        r = subprocess.run(["gcc", "--version"], capture_output=True, text=True, timeout=10)
+        return r.stdout.splitlines()[0].strip() if r.stdout else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
 def run_env(torch):
-    """What the numbers were measured on: device, CU count, ROCm and torch versions, source revision."""
+    """What the numbers were measured on: device, CU count, ROCm and torch versions, host CPU, gcc
+    (which builds the oracle), source revision."""
     env = {"device": torch.cuda.get_device_name(0),
            "cus": torch.cuda.get_device_properties(0).multi_processor_count,
-           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)}
+           "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+           "host_cpu": host_cpu(), "host_threads": os.cpu_count(), "gcc": gcc_version()}
     try:
         with open("/opt/rocm/.info/version") as f:
             env["rocm"] = f.read().strip()
@@ -172,6 +204,21 @@ def run_env(torch):
     return env
 
 
+def trace_summary(path):
+    """Per-kernel count, median, mean, min and max duration (us) of a rocprofv3 kernel-trace CSV."""
+    import csv
+    import statistics
+    by = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = []
+    for name, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        rows.append({"kernel": name, "launches": len(d), "median_us": round(statistics.median(d), 3),
+                     "mean_us": round(statistics.fmean(d), 3), "min_us": round(min(d), 3), "max_us": round(max(d), 3)})
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,7 +229,14 @@ def main():
                     help="extra forms to time (comma list, or 'none')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel launch statistics (median, mean, min, max) of a rocprofv3 kernel "
+                         "trace and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.trace_summary:
+        for r in trace_summary(args.trace_summary):
+            print(json.dumps(r))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
@@ -202,17 +256,19 @@ def main():
     # ---------------- headline: dense self-attention, SDXL level 1
     wl = synth.WORKLOADS["sdxl_l1_self_b2h10s4096"]
     log(f"bench: {wl.desc}")
-    q, k, v = (up(x, torch) for x in synth.make_dense(wl))
-    o = torch.empty_like(q)
+    # 8 input copies (336 MB, past the last-level cache): every step reads its inputs from HBM
+    dsets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s_)] for s_ in range(8)]
+    o = torch.empty_like(dsets[0][0])
     flops = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk)
 
-    def step(_):
-        ka.ka_attn_fwd(q, k, v, o=o, scale=wl.scale)
+    def step(i):
+        ka.ka_attn_fwd(*dsets[i], o=o, scale=wl.scale)
 
     torch.cuda.synchronize()
-    sec = time_launches(step, 1, args.steps, args.warmup, torch)
+    sec = time_launches(step, len(dsets), args.steps, args.warmup, torch)
+    sec_hot = time_launches(step, 1, args.steps, args.warmup, torch)
     value = flops / sec / 1e12
-    log(f"bench: dense {sec * 1e6:.1f} us/launch, {value:.1f} TFLOP/s")
+    log(f"bench: dense {sec * 1e6:.1f} us/launch ({sec_hot * 1e6:.1f} hot), {value:.1f} TFLOP/s")
     traffic = traffic_for("attn_bf16_quad", 1)
     result = {
         "metric": "attention TFLOP/s (% MFMA peak) dense; GB/s (% HBM peak) banded diff-attn",
@@ -224,46 +280,47 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(flops / sec / 1e12, 3),
                      "peak": acc.MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
                      "frac": round(flops / sec / acc.MFMA_BF16_PEAK, 4), "traffic": traffic,
-                     "kernel": "attn_bf16_quad", "flops_per_launch": flops},
+                     "kernel": "attn_bf16_quad", "flops_per_launch": flops, "us": round(sec * 1e6, 3),
+                     "us_hot": round(sec_hot * 1e6, 3), "input_copies": len(dsets)},
     }
-    del q, k, v, o
+    del dsets, o
 
     forms = {}
     wanted = set() if args.forms == "none" else set(args.forms.split(","))
-    # ---------------- cross-attention against 77 keys (HBM-bound: rotate 8 input copies)
-    if "cross" in wanted:
-        wl = synth.WORKLOADS["sdxl_l2_cross_b2h20q1024k77"]
-        log(f"bench: {wl.desc}")
-        sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s)] for s in range(8)]
-        outs = [torch.empty_like(s[0]) for s in sets]
-        f, b = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk), acc.dense_bytes(wl.B, wl.H, wl.Sq, wl.Sk)
-        sec = time_graph(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
-                         args.warmup, torch)
-        forms["cross"] = {"workload": wl.key, "kernel": "xattn_bf16", "us": round(sec * 1e6, 3),
-                          "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
-                          "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
-                          "bound": "hbm", "flops": f, "bytes": b, "input_copies": len(sets)}
-        log(f"bench: cross {forms['cross']}")
-        del sets, outs
-    # ---------------- more conditioning shapes: SDXL level-1 cross (77 keys), the DiT's 257 tokens (streamed)
-    for name, key, kern in (("cross_l1", "sdxl_l1_cross_b2h10q4096k77", "xattn_bf16"),
-                            ("cross_cond257", "sa3_dit_cross_h24q1422k257", "attn_bf16 (keys streamed)")):
+
+    def form(name, wl, kernel, fn, nsets, flops, nbytes, bound, **extra):
+        """Time one form as a HIP-graph replay: over `nsets` rotated input copies (past the 256 MB
+        last-level cache) and, when there are several, hot (one copy again and again)."""
+        rot, hot = time_graph_hot_and_rotated(fn, nsets, args.steps, args.warmup, torch)
+        r = {"workload": wl.key, "kernel": kernel, "us": round(rot * 1e6, 3), "us_hot": round(hot * 1e6, 3),
+             "input_copies": nsets, "bound": bound}
+        if flops:
+            r.update({"TFLOP/s": round(flops / rot / 1e12, 3), "mfma_frac": round(flops / rot / acc.MFMA_BF16_PEAK, 4),
+                      "flops": flops})
+        if nbytes:
+            r.update({"GB/s": round(nbytes / rot / 1e9, 1), "hbm_frac": round(nbytes / rot / acc.HBM_PEAK, 4),
+                      "GB/s_hot": round(nbytes / hot / 1e9, 1), "bytes": nbytes})
+        r.update(extra)
+        forms[name] = r
+        log(f"bench: {name} {r}")
+
+    def copies(nbytes, lo=2, hi=64):
+        return max(lo, min(hi, -(-600_000_000 // nbytes)))  # input copies: 600 MB, past the last-level cache
+
+    # ---------------- cross-attention: 77 context tokens (SDXL levels 2 and 1), 257 conditioning tokens
+    for name, key in (("cross", "sdxl_l2_cross_b2h20q1024k77"), ("cross_l1", "sdxl_l1_cross_b2h10q4096k77"),
+                      ("cross_cond257", "sa3_dit_cross_h24q1422k257")):
         if name not in wanted:
             continue
         wl = synth.WORKLOADS[key]
         log(f"bench: {wl.desc}")
         f, b = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk), acc.dense_bytes(wl.B, wl.H, wl.Sq, wl.Sk)
-        n = max(2, min(64, -(-600_000_000 // b)))  # input copies: 600 MB, past the 256 MB last-level cache
-        sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s)] for s in range(n)]
-        outs = [torch.empty_like(s[0]) for s in sets]
-        sec = time_graph(lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), len(sets), args.steps,
-                         args.warmup, torch)
-        forms[name] = {"workload": wl.key, "kernel": kern, "us": round(sec * 1e6, 3),
-                       "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
-                       "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
-                       "bound": "hbm" if f / b < acc.MFMA_BF16_PEAK / acc.HBM_PEAK else "mfma", "flops": f, "bytes": b,
-                       "input_copies": len(sets)}
-        log(f"bench: {name} {forms[name]}")
+        n = copies(b)
+        sets = [[up(x, torch) for x in synth.make_dense(wl, seed_base=1000 * wl.index + 10 * s_)] for s_ in range(n)]
+        outs = [torch.empty_like(s_[0]) for s_ in sets]
+        kern = "xattn_bf16 (keys in LDS, one pass)" if wl.Sk <= 128 else "xattn_bf16 (keys in LDS, 64-key chunks)"
+        form(name, wl, kern, lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), n, f, b,
+             "hbm" if f / b < acc.MFMA_BF16_PEAK / acc.HBM_PEAK else "mfma")
         del sets, outs
     # ---------------- head dim 512: the SDXL VAE's single-head mid-block attention
     if "vae_mid" in wanted:
@@ -279,68 +336,33 @@ def main():
                             "bound": "mfma", "flops": f}
         log(f"bench: vae_mid {forms['vae_mid']}")
         del q5, k5, v5, o5
-    # ---------------- banded differential attention (HBM-bound: 3 copies = 425 MB > 256 MB cache)
-    if "band" in wanted:
-        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
-        log(f"bench: {wl.desc}")
-        sets = []
-        for s in range(3):
-            ins, prm = synth.make_diff(wl, seed_base=1000 * wl.index + 10 * s)
-            sets.append(([up(x, torch) for x in ins], [up(x, torch) for x in prm]))
-        outs = [torch.empty_like(s[0][0]) for s in sets]
-        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
 
-        def band(i):
-            ins, (a_, g_, b_, l_) = sets[i]
-            ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window)
-
-        sec = time_graph(band, len(sets), args.steps, args.warmup, torch)
-        forms["band_diff"] = {"workload": wl.key, "kernel": "diff_band", "us": round(sec * 1e6, 3),
-                              "GB/s": round(b / sec / 1e9, 1), "hbm_frac": round(b / sec / acc.HBM_PEAK, 4),
-                              "TFLOP/s": round(f / sec / 1e12, 3), "bound": "hbm", "flops": f, "bytes": b,
-                              "input_copies": len(sets), "traffic": traffic_for("diff_band", 1)}
-        log(f"bench: band {forms['band_diff']}")
-        del sets, outs
-    # ---------------- full differential attention (DiT-shaped)
-    if "full" in wanted:
-        wl = synth.WORKLOADS["sa3_dit_fulldiff_h16s1422"]
-        log(f"bench: {wl.desc}")
-        ins, prm = synth.make_diff(wl)
-        ins = [up(x, torch) for x in ins]
-        a_, g_, b_, l_ = (up(x, torch) for x in prm)
-        o = torch.empty_like(ins[0])
-        ws = torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
-                         device="cuda")
-        f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
-        sec = time_graph(lambda i: ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=o, scale=wl.scale,
-                                                      window=wl.window, workspace=ws),
-                         1, args.steps, args.warmup, torch)
-        forms["full_diff"] = {"workload": wl.key, "kernel": "diff_kprep + diff_flash_split", "us": round(sec * 1e6, 3),
-                              "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
-                              "GB/s": round(b / sec / 1e9, 1), "bound": "mfma", "flops": f, "bytes": b}
-        log(f"bench: full {forms['full_diff']}")
-    # ---------------- the model forms: decoder (DyT, 32 rotary dims), DiT (RMSNorm, 32 rotary dims, padded V)
-    if "band_model" in wanted:
-        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
-        log(f"bench: {wl.desc}, decoder form (DyT, 32 rotary dims)")
-        sets = []
-        for s_ in range(3):
+    def diff_sets(wl, n):
+        out = []
+        for s_ in range(n):
             ins, prm = synth.make_diff(wl, seed_base=1000 * wl.index + 10 * s_)
-            sets.append(([up(x, torch) for x in ins], [up(x, torch) for x in prm]))
+            out.append(([up(x, torch) for x in ins], [up(x, torch) for x in prm]))
+        return out
+
+    # ---------------- banded differential attention (HBM-bound: 3 copies = 425 MB > 256 MB cache)
+    if "band" in wanted or "band_model" in wanted:
+        wl = synth.WORKLOADS["sa3_decoder_banddiff_h8s23086w17"]
+        log(f"bench: {wl.desc}")
+        sets = diff_sets(wl, 3)
         outs = [torch.empty_like(s_[0][0]) for s_ in sets]
         f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
-
-        def band_model(i):
-            ins, (a_, g_, b_, l_) = sets[i]
-            ka.ka_diffattn_fwd_ex(*ins, l_, o=outs[i], scale=wl.scale, window=wl.window, qk_norm="dyt", alpha=a_,
-                                  gamma=g_, beta=b_, rotary_dims=32)
-
-        sec = time_graph(band_model, len(sets), args.steps, args.warmup, torch)
-        forms["band_diff_model"] = {"workload": wl.key, "options": "DyT, rotary on 32 of 64 dims",
-                                    "kernel": "diff_band", "us": round(sec * 1e6, 3), "GB/s": round(b / sec / 1e9, 1),
-                                    "hbm_frac": round(b / sec / acc.HBM_PEAK, 4), "bound": "hbm", "bytes": b,
-                                    "input_copies": len(sets)}
-        log(f"bench: band model form {forms['band_diff_model']}")
+        if "band" in wanted:
+            def band(i):
+                ins, (a_, g_, b_, l_) = sets[i]
+                ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window)
+            form("band_diff", wl, "diff_band", band, len(sets), f, b, "hbm", traffic=traffic_for("diff_band", 1))
+        if "band_model" in wanted:
+            def band_model(i):
+                ins, (a_, g_, b_, l_) = sets[i]
+                ka.ka_diffattn_fwd_ex(*ins, l_, o=outs[i], scale=wl.scale, window=wl.window, qk_norm="dyt", alpha=a_,
+                                      gamma=g_, beta=b_, rotary_dims=32)
+            form("band_diff_model", wl, "diff_band", band_model, len(sets), f, b, "hbm",
+                 options="DyT, rotary on 32 of 64 dims")
         del sets, outs
     if "band_fused" in wanted:
         # the decoder form reading q1, k1, v, q2, k2 straight out of one [B, S, 5, H, 64] projection and
@@ -363,35 +385,37 @@ def main():
             ka.ka_diffattn_fwd_ex(*views, l_, o=out.permute(0, 2, 1, 3), scale=wl.scale, window=wl.window,
                                   qk_norm="dyt", alpha=a_, gamma=g_, beta=b_, rotary_dims=32)
 
-        sec = time_graph(band_fused, len(sets), args.steps, args.warmup, torch)
-        forms["band_diff_fused"] = {"workload": wl.key, "options": "DyT, rotary on 32 of 64 dims, inputs read from "
-                                    "a fused [B,S,5,H,64] projection, output written [B,S,H,64]",
-                                    "kernel": "diff_band", "us": round(sec * 1e6, 3), "GB/s": round(b / sec / 1e9, 1),
-                                    "hbm_frac": round(b / sec / acc.HBM_PEAK, 4), "bound": "hbm", "bytes": b,
-                                    "input_copies": len(sets)}
-        log(f"bench: band fused {forms['band_diff_fused']}")
+        form("band_diff_fused", wl, "diff_band", band_fused, len(sets), f, b, "hbm",
+             options="DyT, rotary on 32 of 64 dims, inputs read from a fused [B,S,5,H,64] projection, output "
+                     "written [B,S,H,64]")
         del sets
-    if "full_model" in wanted:
+    # ---------------- full differential attention (DiT-shaped): key prep, then the flash pass
+    if "full" in wanted or "full_model" in wanted:
         wl = synth.WORKLOADS["sa3_dit_fulldiff_h16s1422"]
-        pad = 142
-        log(f"bench: {wl.desc}, DiT form (RMSNorm, 32 rotary dims, last {pad} tokens padded)")
-        ins, _ = synth.make_diff(wl)
-        ins = [up(x, torch) for x in ins]
-        w_, l_ = (up(x, torch) for x in synth.make_model_params(wl.H, 1000 * wl.index + 6))
-        keep = up(synth.make_v_keep(wl.B, wl.Sq, pad), torch)
-        o = torch.empty_like(ins[0])
-        ws = torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
-                         device="cuda")
+        log(f"bench: {wl.desc}")
         f, b = acc.diff_flops(wl.B, wl.H, wl.Sq, wl.window), acc.diff_bytes(wl.B, wl.H, wl.Sq)
-        sec = time_graph(lambda i: ka.ka_diffattn_fwd_ex(*ins, l_, o=o, scale=wl.scale, window=wl.window,
-                                                         qk_norm="rms", rms_weight=w_, rms_eps=1e-6, rotary_dims=32,
-                                                         v_keep=keep, workspace=ws),
-                         1, args.steps, args.warmup, torch)
-        forms["full_diff_model"] = {"workload": wl.key, "options": f"RMSNorm, rotary on 32 of 64 dims, {pad} padded",
-                                    "kernel": "diff_kprep + diff_flash_split", "us": round(sec * 1e6, 3),
-                                    "TFLOP/s": round(f / sec / 1e12, 3),
-                                    "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4), "bound": "mfma", "flops": f}
-        log(f"bench: full model form {forms['full_diff_model']}")
+        n = copies(b + ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), hi=32)
+        sets = diff_sets(wl, n)
+        outs = [torch.empty_like(s_[0][0]) for s_ in sets]
+        wss = [torch.empty(ka.ka_diffattn_workspace_bytes(wl.B, wl.H, wl.Sq, 64, wl.window), dtype=torch.uint8,
+                           device="cuda") for _ in sets]
+        if "full" in wanted:
+            def full(i):
+                ins, (a_, g_, b_, l_) = sets[i]
+                ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window, workspace=wss[i])
+            form("full_diff", wl, "diff_kprep + diff_flash_duo", full, len(sets), f, b, "mfma")
+        if "full_model" in wanted:
+            pad = 142
+            w_, lm_ = (up(x, torch) for x in synth.make_model_params(wl.H, 1000 * wl.index + 6))
+            keep = up(synth.make_v_keep(wl.B, wl.Sq, pad), torch)
+
+            def full_model(i):
+                ins = sets[i][0]
+                ka.ka_diffattn_fwd_ex(*ins, lm_, o=outs[i], scale=wl.scale, window=wl.window, qk_norm="rms",
+                                      rms_weight=w_, rms_eps=1e-6, rotary_dims=32, v_keep=keep, workspace=wss[i])
+            form("full_diff_model", wl, "diff_kprep + diff_flash_duo", full_model, len(sets), f, b, "mfma",
+                 options=f"RMSNorm, rotary on 32 of 64 dims, {pad} padded")
+        del sets, outs, wss
     if forms:
         result["forms"] = forms
 

@@ -505,7 +505,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     }
     // V fragments are read at MFMA slot DUO_VSLOT, after the K fragments have been consumed by the first
     // QK products; steps without QK work start their P.V products at slot 0 and read them up front
-    constexpr int VS = NEXT ? DUO_VSLOT : -1;
+    constexpr int VS = NEXT ? (DUO_VSLOT < 4 * NQB ? DUO_VSLOT : 4 * NQB - 1) : -1;  // before the first P.V
     auto load_v = [&]() {
       // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
       // (keys 4*grp + e of the first 16-key half, then of the second)

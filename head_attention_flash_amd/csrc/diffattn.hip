@@ -44,6 +44,7 @@
 //                      prepared keys and V; branch 2 is subtracted through LDS at the end.
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "ka_attn.h"
 #include "ka_common.hpp"
@@ -116,8 +117,8 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // Normalise (DyT, or RMSNorm over the row's 64 dims held by four lanes), then rotate,
 // 8 rotary pairs (dims d0+e and d0+gap+e, pair index i0+e) of two tensors (parameter
-// sets ta and tb) at the same position p; the angles are shared.
-template <int NORM, int RED>
+// sets ta and tb) at the same position p; the angles are shared.  ONE: tensor a only.
+template <int NORM, int RED, bool ONE = false>
 __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int d0, int gap, int i0,
                                             int p, int ta, int tb, const SharedParams& sp) {
   const float pf = (float)p;
@@ -137,10 +138,10 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sa = __builtin_fmaf(alo[e], alo[e], __builtin_fmaf(ahi[e], ahi[e], sa));
-      sb = __builtin_fmaf(blo[e], blo[e], __builtin_fmaf(bhi[e], bhi[e], sb));
+      if (!ONE) sb = __builtin_fmaf(blo[e], blo[e], __builtin_fmaf(bhi[e], bhi[e], sb));
     }
     ra = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sa), 1.0f / HD, sp.eps));
-    rb = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sb), 1.0f / HD, sp.eps));
+    if (!ONE) rb = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sb), 1.0f / HD, sp.eps));
   }
   const float ka = sp.k2a[ta], kb = sp.k2a[tb];
 #pragma unroll
@@ -155,10 +156,22 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
     // explicit fused forms: every tensor rounds identically, whatever the compiler would contract
     alo[e] = __builtin_fmaf(a0, cs, -(a1 * sn));
     ahi[e] = __builtin_fmaf(a1, cs, a0 * sn);
-    const float b0 = norm(blo[e], tb, dl, kb, rb), b1 = norm(bhi[e], tb, dh, kb, rb);
-    blo[e] = __builtin_fmaf(b0, cs, -(b1 * sn));
-    bhi[e] = __builtin_fmaf(b1, cs, b0 * sn);
+    if (!ONE) {
+      const float b0 = norm(blo[e], tb, dl, kb, rb), b1 = norm(bhi[e], tb, dh, kb, rb);
+      blo[e] = __builtin_fmaf(b0, cs, -(b1 * sn));
+      bhi[e] = __builtin_fmaf(b1, cs, b0 * sn);
+    }
   }
+}
+
+// Two fp32 -> two fp16 in one word, rounded toward zero (v_cvt_pkrtz_f16_f32; a value
+// representable in fp16 converts exactly either way).
+__device__ __forceinline__ unsigned cvt2_f16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ __forceinline__ f16x8 cat_f16(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
@@ -425,295 +438,426 @@ void diff_band(DiffArgs a, int nblk, int nstrip) {
 }
 
 // ---------------------------------------------------------------- full path, pass 1: key prep
+// Eight threads per key row: lanes 0-3 of the octet prepare k1 (8 rotary pairs each), lanes
+// 4-7 k2, and each converts 8 values of V to fp16.  (Four threads per row holding both
+// tensors left about 1.4 waves per SIMD for the 1422-token shape: too few to cover the load
+// and transcendental latencies of this short pass.)
 template <int NORM>
 __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   __shared__ SharedParams sp;
-  load_params<NORM>(sp, a);
-  __syncthreads();
   const size_t nrows = (size_t)a.B * a.H * a.S;
-  const size_t row = (size_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int cc = threadIdx.x & 3;
-  if (row >= nrows) return;  // whole quads: the four lanes of a row leave together
+  const size_t row0 = (size_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const bool live = row0 < nrows;
+  const size_t row = live ? row0 : nrows - 1;  // lanes past the end load a valid row, store nothing
+  const int sub = threadIdx.x & 7, tk = sub >> 2, cc = sub & 3;  // tensor (0: k1, 1: k2), chunk
   const int j = (int)(row % (size_t)a.S);
   const size_t h = (row / a.S) % a.H, bb = row / a.S / a.H;
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), d0 = lo_dim(cc, rot32);
-  float k1lo[8], k1hi[8], k2lo[8], k2hi[8];
-  load_pairs(a.k1 + slice_at(a, TK1, bb, h) + (size_t)j * a.st[TK1], d0, gap, true, k1lo, k1hi);
-  load_pairs(a.k2 + slice_at(a, TK2, bb, h) + (size_t)j * a.st[TK2], d0, gap, true, k2lo, k2hi);
-  prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, sp);
-  _Float16* w1 = a.ws + row * HD;
-  _Float16* w2 = a.ws + nrows * HD + row * HD;
-  st16(w1 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k1lo)));
-  st16(w1 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k1hi)));
-  st16(w2 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2lo)));
-  st16(w2 + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(k2hi)));
-  if (a.v_keep) {  // V with the rows of flagged-out tokens zeroed, for pass 2
-    const unsigned m = a.v_keep[bb * a.S + j] != 0 ? ~0u : 0u;
-    unsigned short* w3 = reinterpret_cast<unsigned short*>(a.ws) + 2 * nrows * HD + row * HD;
-    const unsigned short* vr = a.v + slice_at(a, TV, bb, h) + (size_t)j * a.st[TV];
-    const uint4 x0 = ld16(vr + 16 * cc), x1 = ld16(vr + 16 * cc + 8);
-    st16(w3 + 16 * cc, make_uint4(x0.x & m, x0.y & m, x0.z & m, x0.w & m));
-    st16(w3 + 16 * cc + 8, make_uint4(x1.x & m, x1.y & m, x1.z & m, x1.w & m));
-  }
+  const int t = tk ? TK2 : TK1;
+  // the row's loads are issued before the parameters are staged, so the two latencies overlap
+  float lo[8], hi[8];
+  load_pairs((tk ? a.k2 : a.k1) + slice_at(a, t, bb, h) + (size_t)j * a.st[t], d0, gap, true, lo, hi);
+  // V row: 8 values per thread
+  const unsigned short* vr = a.v + slice_at(a, TV, bb, h) + (size_t)j * a.st[TV];
+  const uint4 vx = ld16(vr + 8 * sub);
+  const bool keep = !a.v_keep || a.v_keep[bb * a.S + j] != 0;
+  load_params<NORM>(sp, a);
+  __syncthreads();
+  if (!live) return;  // whole octets: the lanes of a row leave together
+  prep_pairs2<NORM, RED_QUAD, true>(lo, hi, lo, hi, d0, gap, 8 * cc, j, tk ? 3 : 1, tk ? 3 : 1, sp);
+  _Float16* w = a.ws + (size_t)tk * nrows * HD + row * HD;
+  st16(w + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(lo)));
+  st16(w + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(hi)));
+  // V as fp16 for pass 2's P.V (exact for 2^-14 <= |v| <= 65504: a bf16 value has 8 significant
+  // bits, fp16 11), with the rows of flagged-out tokens zeroed
+  const unsigned m = keep ? ~0u : 0u;
+  float f[8];
+  unpack_bf16x8(make_uint4(vx.x & m, vx.y & m, vx.z & m, vx.w & m), f);
+  st16(a.ws + 2 * nrows * HD + row * HD + 8 * sub,
+       make_uint4(cvt2_f16(f[0], f[1]), cvt2_f16(f[2], f[3]), cvt2_f16(f[4], f[5]), cvt2_f16(f[6], f[7])));
 }
 
-constexpr int DBN = 64;  // keys per tile
+// ---------------------------------------------------------------- full path, pass 2
+// The dense kernel's loop on the prepared fp16 keys, one branch per wave: 2 NB waves per
+// block, 16 NB queries; waves 0..NB-1 run branch 1 and waves NB..2NB-1 branch 2 for the same
+// NB 16-query blocks, so a wave holds one branch's scores, weights and O.  Keys stream in
+// 32-key tiles through a two-deep LDS ring (K1 and K2 one tile ahead, V one tile behind);
+// step t of a wave
+//   * issues the matrix work of S(t+1) = K(t+1) Q^T and of O += V(t-1)^T P(t-1)^T,
+//   * forms the weights of tile t on the vector unit, one weight beside each MFMA, the order
+//     fixed by scheduling barriers,
+//   * stores the staged K1/K2(t+2) and V(t) into the ring slots read last in step t - 1,
+// then the block synchronises once.  Weights are 2^(c s - R) with R at the query's running
+// maximum (in the exp2 domain), so they stay below 2^F_LAZY until a score passes the maximum
+// by F_LAZY: a packed 16-bit maximum over the fp16 weights and a wave-wide vote replace the
+// per-tile maximum, and only a voting wave takes maxima and raises R (per query, from its own
+// scores).  DyT scores spread widely (a standard deviation near 7 in the exp2 domain): with a
+// threshold of 8 a fifth of the wave-steps raise, with 14 about one in thirty; fp16 holds
+// weights up to 2^15.
+// P and V meet as fp16 (the prepared V plane): half the rounding of bf16 weights.  The row sum
+// comes from an all-ones MFMA over the same fp16 weights, so O / l is a convex combination.
+// At the end branch-2 waves leave lambda O2 / l2 in LDS and branch-1 waves subtract it.
+// BAND: keys outside |i - j| <= window are masked and tiles outside the band of the block are
+// skipped (windows too wide for the one-pass band kernel).
+constexpr int FBN = 32;      // keys per tile
+#ifndef F_VSLOT_SET
+#define F_VSLOT_SET 1
+#endif
+#ifndef F_VLEAD_SET
+#define F_VLEAD_SET 1
+#endif
+#ifndef F_STG_SET
+#define F_STG_SET 4
+#endif
+constexpr int F_VSLOT = F_VSLOT_SET;  // MFMA slot after which a step reads its V fragments
+constexpr int F_VLEAD = F_VLEAD_SET;  // vector work runs this many slots ahead of the MFMAs
+constexpr int F_STG = F_STG_SET;      // vector slot at which the staged tiles are stored
+// One 16-query block per wave (32 queries per workgroup: 720 workgroups for 16 heads x 1422
+// tokens, 2.8 per CU) measured faster than two (368 workgroups: 49.5 vs 42.5 us for both passes):
+// the finer grid balances the chip better than the longer steps amortise their latency.
+#ifndef FULL_NQB
+#define FULL_NQB 1
+#endif
+#ifndef FULL_WPE
+#define FULL_WPE 3
+#endif
+constexpr float R_NONE = -1e30f;  // reference of a query that has seen no key (finite: -inf - -inf = NaN)
+constexpr float F_LAZY = 14.0f;   // raise threshold (exp2 domain): weights stay below 2^14
+constexpr unsigned short F_VOTE = 0x7400;  // fp16 bit pattern of 2^14
 
-// ---------------------------------------------------------------- full path, pass 2: building blocks
-// The dense kernel's pipelined loop (S(t+1) and P.V(t-1) on the matrix core around the
-// softmax of tile t; buffer loads; row sums from an all-ones MFMA; lazily raised
-// maxima) on prepared fp16 keys against the prepared queries, one branch per wave.
-// BAND: keys outside |i - j| <= window are masked and whole tiles outside the band of
-// the workgroup are skipped (windows too wide for the one-pass band kernel).
-template <int NQB>
-__device__ __forceinline__ void dpipe_qk(const unsigned short* Kt, const f16x8 (&Qf)[NQB][2], int col, int grp,
-                                         f32x4 (&S)[4][NQB]) {
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 8 * grp]);
-    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 32 + 8 * grp]);
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      S[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      S[kb][i] = mfma_f16(a1, Qf[i][1], S[kb][i]);
-    }
-  }
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+// Some fp16 half of the four words is >= 2^F_LAZY (non-negative fp16 values order like their
+// bit patterns): a packed maximum, then a saturating subtraction of F_VOTE - 1.
+__device__ __forceinline__ bool any_f16_at_least_vote(unsigned a, unsigned b, unsigned c, unsigned d) {
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, c), __builtin_bit_cast(u16x2, d)));
+  const u16x2 r = __builtin_elementwise_sub_sat(m, u16x2{(unsigned short)(F_VOTE - 1), (unsigned short)(F_VOTE - 1)});
+  return __builtin_bit_cast(unsigned, r) != 0;
 }
 
-// Softmax of one branch's tile against its lazily raised maxima; packs bf16 weights into
-// P and returns whether any maximum was raised (alpha = rescale factors).
-template <int NQB, bool MASK, bool BAND>
-__device__ __forceinline__ bool dpipe_softmax(f32x4 (&S)[4][NQB], int j0, int Slen, int window, int q0, float c,
-                                              int col, int grp, float (&m)[NQB], float (&alpha)[NQB],
-                                              bf16x8 (&P)[2][NQB]) {
-  if (MASK || BAND) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 16 * kb + 4 * grp + e;
-#pragma unroll
-        for (int i = 0; i < NQB; ++i) {
-          const int p = q0 + 16 * i + col;
-          const bool ok = (!MASK || j < Slen) && (!BAND || (j >= p - window && j <= p + window));
-          S[kb][i][e] = ok ? S[kb][i][e] : -INFINITY;
-        }
-      }
-  }
-  bool any = false;
-#pragma unroll
-  for (int i = 0; i < NQB; ++i) {
-    float mx = S[0][i][0];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb][i][e]);
-    mx = group4_max(mx);
-    const bool raise = (mx - m[i]) * c > LAZY_LOG2;  // false for a row that has seen no key
-    const float mnew = raise ? mx : m[i];
-    alpha[i] = raise ? fast_exp2((m[i] - mnew) * c) : 1.0f;
-    m[i] = mnew;
-    any = any || raise;
-    const float mc = (BAND && mnew == -INFINITY) ? 0.0f : mnew * c;  // no key yet: all weights 0
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[kb][i][e] = fast_exp2(__builtin_fmaf(S[kb][i][e], c, -mc));
-  }
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      P[ks][i] = pack_bf16(S[2 * ks][i], S[2 * ks + 1][i]);
-      asm volatile("" : "+v"(P[ks][i]));  // materialise here, not past the rescale branch
-    }
-  return any;
+// Workgroup b of n runs on XCD b % 8: the first 8 floor(n / 8) workgroups are renumbered so that
+// XCD x takes a contiguous run of items.
+__device__ __forceinline__ int xcd_major(int blk, int n) {
+  const int n8 = n & ~7;
+  return blk < n8 ? (blk & 7) * (n8 >> 3) + (blk >> 3) : blk;
 }
 
-// ---------------------------------------------------------------- full path, pass 2: one branch per wave
-// Eight waves per block, 64 queries: waves 0-3 run branch 1 and waves 4-7 branch 2 for the
-// same four 16-query blocks, so a wave holds one branch's scores, weights and O (about half
-// the registers of a two-branch wave) and twice as many waves share the work; the block
-// stages K1, K2 and V tiles (one 16-byte chunk of each per thread and tile).  At the end
-// branch-2 waves leave lambda O2 / l2 in LDS and branch-1 waves subtract it.
-template <bool BAND, int NORM>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void diff_flash_split(DiffArgs a, int nqb) {
-  __shared__ __align__(16) unsigned short K1b[2][DBN * KPD];
-  __shared__ __align__(16) unsigned short K2b[2][DBN * KPD];
-  __shared__ __align__(16) unsigned short Vb[2][DBN * VPD];
+struct FullLds {
+  unsigned short K1[2][FBN * KPD];
+  unsigned short K2[2][FBN * KPD];
+  unsigned short V[2][FBN * VPD];
+};
+
+template <bool BAND, int NORM, int NQB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FULL_WPE, FULL_WPE)))
+void diff_flash_duo(DiffArgs a, int nqb) {
+  constexpr int QPW = 16 * NQB;    // queries of a wave
+  constexpr int QWG = 2 * QPW;     // queries of a block (two waves per branch)
+  static_assert(FBN * 8 == 256, "one 16-byte chunk of each tensor per thread and tile");
+  static_assert(2 * 2 * FBN * KPD * 2 >= 2 * NQB * 4 * 64 * 16, "the branch-2 hand-over must fit the K rings");
+  __shared__ __align__(16) FullLds sm;
   __shared__ SharedParams sp;
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int br = w >> 2;  // 0: branch 1, 1: branch 2 (wave-uniform)
+  const int br = w >> 1;  // 0: branch 1, 1: branch 2 (wave-uniform)
+  const int wq = w & 1;   // which half of the block's queries
   const int S = a.S, window = a.window;
-  const size_t bh = blockIdx.x / nqb;  // one-dimensional grid: (b, h) major, 64-query block minor
+  // Workgroups are dispatched round-robin over the 8 XCDs (block b on XCD b % 8), each with its
+  // own L2: items are numbered XCD-major, so the blocks of one (b, h) -- which all stream that
+  // head's prepared keys and V -- share one L2.
+  const int item = xcd_major(blockIdx.x, gridDim.x);
+  const size_t bh = item / nqb;  // items: (b, h) major, query block minor
   const int h = (int)(bh % a.H);
   const size_t bb = bh / a.H;
   const size_t base = bh * (size_t)S * HD;  // of the workspace's contiguous planes
   const size_t nrows = (size_t)a.B * a.H * S;
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), qd0 = lo_dim(grp, rot32);
-  load_params<NORM>(sp, a);
-  __syncthreads();
+  const float c = a.c;
 
-  const int qblk0 = (blockIdx.x % nqb) * 64;
-  const int q0 = qblk0 + 16 * (w & 3);
-  const int p = q0 + col;
-  f16x8 Qf[1][2];
+  const int qa = (item % nqb) * QWG, qb_ = min(S - 1, qa + QWG - 1);
+  const int q0 = qa + QPW * wq;  // first query of this wave; block i holds q0 + 16 i + col
+  f16x8 Qf[NQB][2];
   {
-    // this branch's query (q1 with set 0, or q2 with set 2); prepared twice over so that the
-    // two-tensor preparation serves one tensor
+    // this branch's queries (q1 with set 0, or q2 with set 2), requested before the parameters
+    // are staged so that the two latencies overlap
     const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
     const unsigned short* qt = br ? a.q2 : a.q1;
-    float lo[8], hi[8], lo2[8], hi2[8];
-    const size_t pc = p < S ? p : 0;
-    load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo, hi);
+    float lo[NQB][8], hi[NQB][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo2[e] = lo[e];
-      hi2[e] = hi[e];
+    for (int i = 0; i < NQB; ++i) {
+      const int p = q0 + 16 * i + col;
+      const size_t pc = p < S ? p : 0;
+      load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo[i], hi[i]);
     }
-    prep_pairs2<NORM, RED_GROUP4>(lo, hi, lo2, hi2, qd0, gap, 8 * grp, p, set, set, sp);
-    Qf[0][0] = to_f16x8(lo);
-    Qf[0][1] = to_f16x8(hi);
+    load_params<NORM>(sp, a);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      prep_pairs2<NORM, RED_GROUP4, true>(lo[i], hi[i], lo[i], hi[i], qd0, gap, 8 * grp, q0 + 16 * i + col, set, set,
+                                          sp);
+      Qf[i][0] = to_f16x8(lo[i]);
+      Qf[i][1] = to_f16x8(hi[i]);
+    }
   }
-  f32x4 O[4], L = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int db = 0; db < 4; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[1] = {-INFINITY};
-  bf16x8 P[2][1];
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
-  int t_lo = 0, t_hi = (S - 1) / DBN;
+  int t_lo = 0, t_hi = (S - 1) / FBN;
   if (BAND) {
-    const int qlast = min(S - 1, qblk0 + 63);
-    t_lo = max(0, qblk0 - window) / DBN;
-    t_hi = min(S - 1, qlast + window) / DBN;
+    t_lo = max(0, qa - window) / FBN;
+    t_hi = min(S - 1, qb_ + window) / FBN;
   }
   const int T = t_hi - t_lo + 1;
   const int rbytes = S * HD * 2;
-  const unsigned short* k1h = reinterpret_cast<const unsigned short*>(a.ws) + base;
-  const unsigned short* k2h = reinterpret_cast<const unsigned short*>(a.ws) + nrows * HD + base;
-  const unsigned short* vsrc =
-      a.v_keep ? reinterpret_cast<const unsigned short*>(a.ws) + 2 * nrows * HD + base : a.v + slice_at(a, TV, bb, h);
-  const int vrowb = a.v_keep ? HD * 2 : 2 * a.st[TV];
-  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes);
-  const rsrc_t vrs = make_rsrc(vsrc, a.v_keep ? rbytes : slice_bytes(a, TV));
-  // one chunk per thread and tile: row tid / 8, 16-byte column tid % 8
+  const _Float16* k1h = a.ws + base;
+  const _Float16* k2h = a.ws + nrows * HD + base;
+  const _Float16* vh = a.ws + 2 * nrows * HD + base;
+  // rows past S read as zero through the buffer resources
+  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(vh, rbytes);
+  // staging: thread tid moves row tid / 8, 16-byte column tid % 8 of each tensor's tile
   const int srow = tid >> 3, scol = (tid & 7) * 8;
-  auto gld = [&](const rsrc_t& src, int u, int rowb) {
-    return buf_ld16(src, ((t_lo + u) * DBN + srow) * rowb + (tid & 7) * 16);
-  };
-  unsigned short(*Kr)[DBN * KPD] = br ? K2b : K1b;  // this wave's branch keys
+  auto ld = [&](const rsrc_t& r, int u) { return buf_ld16(r, ((t_lo + u) * FBN + srow) * (HD * 2) + (tid & 7) * 16); };
+  const unsigned short(*Kr)[FBN * KPD] = br ? sm.K2 : sm.K1;  // this wave's branch keys
 
-  f32x4 Sa[4][1], Sb[4][1];
-  st16(&K1b[0][srow * KPD + scol], gld(k1rs, 0, HD * 2));
-  st16(&K2b[0][srow * KPD + scol], gld(k2rs, 0, HD * 2));
-  __syncthreads();
-  dpipe_qk<1>(Kr[0], Qf, col, grp, Sa);
-  if (T > 1) {
-    st16(&K1b[1][srow * KPD + scol], gld(k1rs, 1, HD * 2));
-    st16(&K2b[1][srow * KPD + scol], gld(k2rs, 1, HD * 2));
+  f32x4 O[4][NQB], L[NQB];
+  float R[NQB];
+  f16x8 P[NQB];
+#pragma unroll
+  for (int i = 0; i < NQB; ++i) {
+    R[i] = R_NONE;
+    L[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) O[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+
+  uint4 stk1, stk2, stv;
+  f32x4 Sa[2][NQB], Sb[2][NQB];
+  // prologue: K(0) -> ring 0, S(0) = K(0) Q^T; K(1) -> ring 1; stage K(2) and V(0)
+  st16(&sm.K1[0][srow * KPD + scol], ld(k1rs, 0));
+  st16(&sm.K2[0][srow * KPD + scol], ld(k2rs, 0));
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kr[0][(16 * kb + col) * KPD + 8 * grp]);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kr[0][(16 * kb + col) * KPD + 32 + 8 * grp]);
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      Sa[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      Sa[kb][i] = mfma_f16(a1, Qf[i][1], Sa[kb][i]);
+    }
+  }
+  if (T > 1) {
+    st16(&sm.K1[1][srow * KPD + scol], ld(k1rs, 1));
+    st16(&sm.K2[1][srow * KPD + scol], ld(k2rs, 1));
+  }
+  stk1 = ld(k1rs, 2);  // past the last tile: zeros, never stored
+  stk2 = ld(k2rs, 2);
+  stv = ld(vrs, 0);
   __syncthreads();
 
-  auto step = [&](auto has_next, auto has_prev, int u, f32x4 (&Sc)[4][1], f32x4 (&Sn)[4][1]) {
+  auto step = [&](auto has_next, auto has_prev, auto parity, int t, f32x4 (&Sc)[2][NQB], f32x4 (&Sn)[2][NQB]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
-    uint4 r1, r2;
+    constexpr int PAR = decltype(parity)::value;  // t & 1
+    f16x8 kf[2][2], vf[4];
     if (NEXT) {
-      r1 = gld(k1rs, u + 2, HD * 2);  // past the last tile: zeros, never written
-      r2 = gld(k2rs, u + 2, HD * 2);
+      const unsigned short* Kt = Kr[PAR ^ 1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          kf[kb][hh] = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 32 * hh + 8 * grp]);
     }
-    const uint4 rv = gld(vrs, u, vrowb);
-    if (NEXT) dpipe_qk<1>(Kr[(u + 1) & 1], Qf, col, grp, Sn);
-    if (PREV) {  // P.V of tile u - 1 (one branch) and its row sums
-      const unsigned short* Vt = Vb[(u - 1) & 1];
+    // V fragments are read right after MFMA slot VS, before the first P.V product (slot NQK);
+    // steps without QK work start their P.V products at slot 0 and read them up front
+    constexpr int NQK = NEXT ? 4 * NQB : 0;
+    constexpr int VS = NEXT ? (F_VSLOT < NQK ? F_VSLOT : NQK - 1) : -1;
+    auto load_v = [&]() {
+      // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
+      const unsigned short* Vt = sm.V[PAR ^ 1];
+      const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int vrow = 32 * ks + 4 * grp + (col >> 2);
+      for (int db = 0; db < 4; ++db) {
+        const int vcol = 16 * db + 4 * (col & 3);
+        vf[db] = cat_f16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
+      }
+    };
+    if (PREV && VS < 0) load_v();
+    // keys past S (last tile) or outside the band of some query of the block take no weight
+    const int j0 = (t_lo + t) * FBN;
+    const bool edge = j0 + FBN > S || (BAND && !(j0 >= qb_ - window && j0 + FBN - 1 <= qa + window));
+    if (edge) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int vcol = 16 * db + 4 * (col & 3);
-          const bf16x8 av =
-              cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
-          O[db] = mfma_bf16(av, P[ks][0], O[db]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + 16 * kb + 4 * grp + e;
+#pragma unroll
+          for (int i = 0; i < NQB; ++i) {
+            const int p = q0 + 16 * i + col;
+            const bool ok = j < S && (!BAND || (j >= p - window && j <= p + window));
+            Sc[kb][i][e] = ok ? Sc[kb][i][e] : -INFINITY;
+          }
         }
-        L = mfma_bf16(ones, P[ks][0], L);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NM = NQK + (PREV ? 5 * NQB : 0);
+    auto mfma_at = [&](auto jj) {
+      constexpr int j = decltype(jj)::value;
+      if constexpr (j < NQK) {
+        constexpr int i = j / 4, kb = (j / 2) % 2, hh = j % 2;
+        if constexpr (hh == 0)
+          Sn[kb][i] = mfma_f16(kf[kb][0], Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f});
+        else
+          Sn[kb][i] = mfma_f16(kf[kb][1], Qf[i][1], Sn[kb][i]);
+      } else if constexpr (j < NM) {
+        constexpr int jp = j - NQK, i = jp / 5, db = jp % 5;
+        if constexpr (db < 4)
+          O[db][i] = mfma_f16(vf[db], P[i], O[db][i]);
+        else
+          L[i] = mfma_f16(ones, P[i], L[i]);
+      }
+    };
+    unsigned Pw[NQB][4];
+    float xe[NQB];
+    bool vote = false;
+    auto valu_at = [&](auto ss) {
+      constexpr int sidx = decltype(ss)::value;
+      constexpr int i = sidx / 9, e = sidx % 9;
+      if constexpr (i < NQB) {
+        if constexpr (e < 8) {
+          float x = fast_exp2(__builtin_fmaf(Sc[e >> 2][i][e & 3], c, -R[i]));
+          asm volatile("" : "+v"(x));  // computed in its slot, not sunk past the next barrier
+          if constexpr (e & 1) {
+            Pw[i][e >> 1] = cvt2_f16(xe[i], x);
+            asm volatile("" : "+v"(Pw[i][e >> 1]));
+          } else {
+            xe[i] = x;
+          }
+        } else {
+          vote = vote || any_f16_at_least_vote(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]);
+        }
+      }
+    };
+    // slot s: MFMA s - F_VLEAD, then vector work s (8 weights per query block, packed in pairs,
+    // and the block's vote test)
+    constexpr int NSLOT = (NM + F_VLEAD > 9 * NQB) ? NM + F_VLEAD : 9 * NQB;
+    [&]<int... SL>(std::integer_sequence<int, SL...>) {
+      ([&] {
+        constexpr int SM = SL - F_VLEAD;
+        if constexpr (SM >= 0) mfma_at(std::integral_constant<int, SM>{});
+        if constexpr (PREV && VS >= 0 && SM == VS) load_v();
+        if constexpr (SL == (F_STG < NSLOT ? F_STG : NSLOT - 1)) {
+          // the ring slots written here were last read in step t - 1
+          if (t + 2 < T) {
+            st16(&sm.K1[PAR][srow * KPD + scol], stk1);
+            st16(&sm.K2[PAR][srow * KPD + scol], stk2);
+          }
+          st16(&sm.V[PAR][srow * VPD + scol], stv);
+          stk1 = ld(k1rs, t + 3);  // past the last tile: zeros, never stored
+          stk2 = ld(k2rs, t + 3);
+          stv = ld(vrs, t + 1);
+        }
+        valu_at(std::integral_constant<int, SL>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }(), ...);
+    }(std::make_integer_sequence<int, NSLOT>{});
+    // some weight of this tile reached 2^F_LAZY, or first tile
+    const bool raised = !PREV || __builtin_amdgcn_ballot_w64(vote) != 0;
+    if (raised) {
+#pragma unroll
+      for (int i = 0; i < NQB; ++i) {
+        // R moves only for a query whose own largest weight 2^(c max - R) reached 2^F_LAZY (a
+        // query that has seen no key keeps R_NONE and weight 0), so a query's result depends on
+        // its own scores
+        const float lmx = fmaxf(fmaxf(fmaxf(Sc[0][i][0], Sc[0][i][1]), fmaxf(Sc[0][i][2], Sc[0][i][3])),
+                                fmaxf(fmaxf(Sc[1][i][0], Sc[1][i][1]), fmaxf(Sc[1][i][2], Sc[1][i][3])));
+        const float gmx = group4_max(lmx);
+        const float Rn = __builtin_fmaf(gmx, c, -R[i]) >= F_LAZY ? gmx * c : R[i];
+        const float alpha = fast_exp2(R[i] - Rn);  // 0 on a query's first keys, 1 where R stays
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+          Pw[i][hh] = cvt2_f16(fast_exp2(__builtin_fmaf(Sc[hh >> 1][i][2 * (hh & 1)], c, -Rn)),
+                               fast_exp2(__builtin_fmaf(Sc[hh >> 1][i][2 * (hh & 1) + 1], c, -Rn)));
+        R[i] = Rn;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) O[db][i] *= alpha;
+        L[i] *= alpha;
       }
     }
-    const int j0 = (t_lo + u) * DBN;
-    float al[1];
-    const bool any = j0 + DBN > S ? dpipe_softmax<1, true, BAND>(Sc, j0, S, window, q0, a.c, col, grp, m, al, P)
-                                  : dpipe_softmax<1, false, BAND>(Sc, j0, S, window, q0, a.c, col, grp, m, al, P);
-    if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) O[db] *= al[0];
-      L *= al[0];
-    }
-    if (NEXT && u + 2 < T) {
-      st16(&K1b[u & 1][srow * KPD + scol], r1);
-      st16(&K2b[u & 1][srow * KPD + scol], r2);
-    }
-    st16(&Vb[u & 1][srow * VPD + scol], rv);
+    for (int i = 0; i < NQB; ++i) P[i] = __builtin_bit_cast(f16x8, make_uint4(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]));
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   if (T == 1) {
-    step(no{}, no{}, 0, Sa, Sb);
+    step(no{}, no{}, P0{}, 0, Sa, Sb);
   } else {
-    step(yes{}, no{}, 0, Sa, Sb);
-    int u = 1;
-    for (; u + 2 <= T - 1; u += 2) {
-      step(yes{}, yes{}, u, Sb, Sa);
-      step(yes{}, yes{}, u + 1, Sa, Sb);
+    step(yes{}, no{}, P0{}, 0, Sa, Sb);
+    int t = 1;
+    for (; t + 2 <= T - 1; t += 2) {
+      step(yes{}, yes{}, P1{}, t, Sb, Sa);
+      step(yes{}, yes{}, P0{}, t + 1, Sa, Sb);
     }
-    if (u < T - 1) {
-      step(yes{}, yes{}, u, Sb, Sa);
-      step(no{}, yes{}, u + 1, Sa, Sb);
+    if (t < T - 1) {
+      step(yes{}, yes{}, P1{}, t, Sb, Sa);
+      step(no{}, yes{}, P0{}, t + 1, Sa, Sb);
     } else {
-      step(no{}, yes{}, u, Sb, Sa);
+      step(no{}, yes{}, P1{}, t, Sb, Sa);
     }
   }
   {  // P.V of the last tile
-    const unsigned short* Vt = Vb[(T - 1) & 1];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int vrow = 32 * ks + 4 * grp + (col >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int vcol = 16 * db + 4 * (col & 3);
-        const bf16x8 av = cat_bf16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
-        O[db] = mfma_bf16(av, P[ks][0], O[db]);
-      }
-      L = mfma_bf16(ones, P[ks][0], L);
-    }
-  }
-  // branch 2 leaves lambda O2 / l2 in LDS (over the K1 tiles, no longer read after the last
-  // barrier); branch 1 subtracts it from O1 / l1
-  f32x4* X = reinterpret_cast<f32x4*>(&K1b[0][0]);  // [4 blocks][4 dim groups][64 lanes]
-  if (br) {
-    const float i2 = a.lambda[h] / L[0];
-#pragma unroll
-    for (int db = 0; db < 4; ++db) X[((w & 3) * 4 + db) * 64 + lane] = f32x4{pin(O[db][0] * i2), pin(O[db][1] * i2),
-                                                                             pin(O[db][2] * i2), pin(O[db][3] * i2)};
-  }
-  __syncthreads();
-  if (!br && p < S) {
-    const float i1 = 1.0f / L[0];
-    unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
+    const unsigned short* Vt = sm.V[(T - 1) & 1];
+    const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const f32x4 x = X[((w & 3) * 4 + db) * 64 + lane];
-      f32x4 r;
+      const int vcol = 16 * db + 4 * (col & 3);
+      const f16x8 av = cat_f16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = pin(O[db][e] * i1) - x[e];
-      st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
+      for (int i = 0; i < NQB; ++i) O[db][i] = mfma_f16(av, P[i], O[db][i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) L[i] = mfma_f16(ones, P[i], L[i]);
+  }
+  // branch 2 leaves lambda O2 / l2 in LDS (over the K rings, no longer read after the last
+  // barrier); branch 1 subtracts it from O1 / l1
+  f32x4* X = reinterpret_cast<f32x4*>(&sm.K1[0][0]);  // [2 waves][NQB blocks][4 dim groups][64 lanes]
+  const float lam = a.lambda[h];
+  if (br) {
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      const float i2 = lam / L[i][0];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        X[((wq * NQB + i) * 4 + db) * 64 + lane] = f32x4{pin(O[db][i][0] * i2), pin(O[db][i][1] * i2),
+                                                         pin(O[db][i][2] * i2), pin(O[db][i][3] * i2)};
+    }
+  }
+  __syncthreads();
+  if (!br) {
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      const int p = q0 + 16 * i + col;
+      if (p < S) {
+        const float i1 = 1.0f / L[i][0];
+        unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const f32x4 x = X[((wq * NQB + i) * 4 + db) * 64 + lane];
+          f32x4 r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = pin(O[db][i][e] * i1) - x[e];
+          st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
+        }
+      }
     }
   }
 }
@@ -721,10 +865,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // ---------------------------------------------------------------- dispatch
 static bool use_band(int S, int window) { return window >= 0 && window < S - 1 && window <= BAND_MAX_WINDOW; }
 
-// full path: k1^, k2^ (fp16) and, for calls with V flags, the flagged V (bf16)
+// full path: k1^, k2^ and V (with flagged rows zeroed), all fp16
 size_t diff_workspace_bytes(int B, int H, int S, int window, bool v_flags) {
+  (void)v_flags;
   if (use_band(S, window)) return 0;
-  return (size_t)(v_flags ? 3 : 2) * B * H * S * HD * sizeof(_Float16);
+  return (size_t)3 * B * H * S * HD * sizeof(_Float16);
 }
 
 // ---------------------------------------------------------------- allocation-free workspace
@@ -782,25 +927,26 @@ hipError_t launch_diffattn(const DiffArgs& a0, hipStream_t s) {
     return hipGetLastError();
   }
   const size_t nrows = (size_t)BH * a.S;
-  const dim3 kgrid((unsigned)((nrows + 63) / 64));
+  const dim3 kgrid((unsigned)((nrows + 31) / 32));
   if (a.norm == NORM_RMS)
     hipLaunchKernelGGL(diff_kprep<NORM_RMS>, kgrid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(diff_kprep<NORM_DYT>, kgrid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqb = (a.S + 63) / 64;
+  constexpr int NQB = FULL_NQB, QWG = 32 * NQB;  // query blocks per wave, queries per workgroup
+  const int nqb = (a.S + QWG - 1) / QWG;
   const dim3 grid(nqb * BH);
   if (a.norm == NORM_RMS) {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash_split<true, NORM_RMS>), grid, dim3(512), 0, s, a, nqb);
+      hipLaunchKernelGGL((diff_flash_duo<true, NORM_RMS, NQB>), grid, dim3(256), 0, s, a, nqb);
     else
-      hipLaunchKernelGGL((diff_flash_split<false, NORM_RMS>), grid, dim3(512), 0, s, a, nqb);
+      hipLaunchKernelGGL((diff_flash_duo<false, NORM_RMS, NQB>), grid, dim3(256), 0, s, a, nqb);
   } else {
     if (a.window >= 0)
-      hipLaunchKernelGGL((diff_flash_split<true, NORM_DYT>), grid, dim3(512), 0, s, a, nqb);
+      hipLaunchKernelGGL((diff_flash_duo<true, NORM_DYT, NQB>), grid, dim3(256), 0, s, a, nqb);
     else
-      hipLaunchKernelGGL((diff_flash_split<false, NORM_DYT>), grid, dim3(512), 0, s, a, nqb);
+      hipLaunchKernelGGL((diff_flash_duo<false, NORM_DYT, NQB>), grid, dim3(256), 0, s, a, nqb);
   }
   return hipGetLastError();
 }

@@ -114,6 +114,10 @@ ka_status ka_xattn_fwd(ka_dtype dtype, const void* q, const void* k, const void*
  *   dyt_alpha [4], dyt_gamma [4][64], dyt_beta [4][64], lambda [H]: fp32 device.
  *   workspace: device scratch of at least ka_diffattn_workspace_bytes(B,H,S,D,
  *   window) bytes (may be NULL when that is 0); its contents are overwritten.
+ * Precision: DyT, rotation, softmax and the subtraction in fp32; q^, k^ enter Q K^T as
+ * fp16.  Banded path: weights bf16 against bf16 V.  Full and wide-window path: weights
+ * and V as fp16, so V must lie within fp16 range, |v| <= 65504 (larger values saturate
+ * to 65504; values below 2^-14 keep an absolute error under 2^-24).
  */
 ka_status ka_diffattn_fwd(ka_dtype dtype, const void* q1, const void* k1, const void* q2, const void* k2,
                           const void* v, void* o, int B, int H, int Sq, int Sk, int D, float scale, int window,
@@ -191,10 +195,10 @@ ka_status ka_diffattn_fwd_noalloc(ka_dtype dtype, const void* q1, const void* k1
                                   const ka_layout* layouts, hipStream_t stream);
 
 /* Workspace bytes ka_diffattn_fwd and ka_diffattn_fwd_ex need for this shape: 0 for
- * the banded path; for the full path the prepared keys (2*B*H*S*64 fp16) plus room
- * for a flagged copy of V (B*H*S*64 bf16), which only calls with v_keep use (without
- * v_keep the first 2*B*H*S*64*2 bytes suffice).  Returns 0 for invalid shapes as
- * well; the call then reports the error. */
+ * the banded path; for the full (and wide-window) path three fp16 planes of B*H*S*64:
+ * the prepared keys k1^ and k2^, and V converted to fp16 (rows of tokens flagged out by
+ * v_keep zeroed).  Returns 0 for invalid shapes as well; the call then reports the
+ * error. */
 size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window);
 
 /* Name of the kernel (and query layout) ka_attn_fwd launches for this shape on the

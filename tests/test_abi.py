@@ -109,9 +109,9 @@ def test_diff_validation(lib):
     assert diff(lib, scale=-1.0) == _lib.KA_ERR_PARAM
     assert diff(lib, v=A + 4) == _lib.KA_ERR_ALIGN
     assert diff(lib, o=Q + 64) == _lib.KA_ERR_ALIAS
-    # the full path needs a workspace: the prepared keys (the reported size also covers a flagged V)
+    # the full path needs a workspace: the prepared keys and V, three fp16 planes
     assert lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1) == 3 * 1 * 2 * 8 * 64 * 2
-    need = 2 * 1 * 2 * 8 * 64 * 2
+    need = 3 * 1 * 2 * 8 * 64 * 2
     assert diff(lib, window=-1) == _lib.KA_ERR_NULL
     assert diff(lib, window=-1, ws=W, ws_bytes=need - 1) == _lib.KA_ERR_WORKSPACE
     assert diff(lib, window=-1, ws=W + 8, ws_bytes=need) == _lib.KA_ERR_ALIGN
@@ -146,7 +146,7 @@ def test_diff_ex_validation(lib):
     assert diff_ex(lib, Sk=9) == _lib.KA_ERR_SHAPE
     assert diff_ex(lib, D=128) == _lib.KA_ERR_UNSUPPORTED
     assert diff_ex(lib, o=KEEP) == _lib.KA_ERR_ALIAS  # o over the V flags
-    # with V flags the full path needs the larger workspace
+    # the full path's workspace, with or without V flags
     need3 = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
     assert diff_ex(lib, window=-1, ws=W, ws_bytes=need3 - 1) == _lib.KA_ERR_WORKSPACE
     assert diff_ex(lib, window=-1, ws=KEEP - need3 + 16, ws_bytes=need3) == _lib.KA_ERR_ALIAS
@@ -215,10 +215,10 @@ def test_parameter_arrays_may_not_overlap_outputs(lib):
     assert diff(lib, lam=O + 1024) == _lib.KA_ERR_ALIAS
     assert diff_ex(lib, rms_w=O + 32) == _lib.KA_ERR_ALIAS
     # ... and the workspace over any of them (the full path)
-    need = 2 * 1 * 2 * 8 * 64 * 2  # the prepared keys: all a call without V flags uses
+    need = lib.ka_diffattn_workspace_bytes(1, 2, 8, 64, -1)
     assert diff(lib, window=-1, ws=G - 64, ws_bytes=need) == _lib.KA_ERR_ALIAS
     assert diff(lib, window=-1, ws=L - need + 16, ws_bytes=need) == _lib.KA_ERR_ALIAS
-    assert diff_ex(lib, window=-1, ws=G - 16, ws_bytes=3 * need // 2) == _lib.KA_ERR_ALIAS
+    assert diff_ex(lib, window=-1, ws=G - 16, ws_bytes=need) == _lib.KA_ERR_ALIAS
     assert lib.ka_last_hip_error() == 0
 
 
