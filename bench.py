@@ -134,7 +134,7 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, launch_units):
+def traffic_for(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it still matches the source."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -204,6 +204,62 @@ def run_env(torch):
     return env
 
 
+# kernels whose HBM traffic profiles/traffic.json records, and the sources each is built from
+KERNEL_SOURCES = {
+    "attn_bf16_quad": ["head_attention_flash_amd/csrc/attn_dense.hip", "head_attention_flash_amd/csrc/ka_common.hpp"],
+    "xattn_bf16": ["head_attention_flash_amd/csrc/attn_dense.hip", "head_attention_flash_amd/csrc/ka_common.hpp"],
+    "diff_band": ["head_attention_flash_amd/csrc/diffattn.hip", "head_attention_flash_amd/csrc/ka_common.hpp"],
+    "diff_kprep": ["head_attention_flash_amd/csrc/diffattn.hip", "head_attention_flash_amd/csrc/ka_common.hpp"],
+    "diff_flash_duo": ["head_attention_flash_amd/csrc/diffattn.hip", "head_attention_flash_amd/csrc/ka_common.hpp"],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def short_kernel(name):
+    for k in list(KERNEL_SOURCES) + [COPY_KERNEL]:
+        if k in name:
+            return k
+    return name
+
+
+def counter_values(path):
+    """{kernel: {counter: {dispatch id: value}}} from a rocprofv3 counter-collection CSV (a counter's
+    values over the instances of one dispatch are summed)."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = acc.setdefault(short_kernel(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return acc
+
+
+def counter_means(path):
+    """{kernel: {counter: mean value per dispatch}}, {kernel: dispatches}."""
+    acc = counter_values(path)
+    means = {k: {c: sum(v.values()) / len(v) for c, v in d.items()} for k, d in acc.items()}
+    return means, {k: max(len(v) for v in d.values()) for k, d in acc.items()}
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two runs), each scaled by
+    what the same counter reads for the plain 256 MiB device copy that --copy-calibration launches."""
+    fetch, nf = counter_means(fetch_csv)
+    write, nw = counter_means(write_csv)
+    copy_bytes = 256 << 20
+    # the calibration copy is the largest copy dispatch (input uploads run the same copy kernel)
+    cf = max(counter_values(fetch_csv)[COPY_KERNEL]["FETCH_SIZE"].values())
+    cw = max(counter_values(write_csv)[COPY_KERNEL]["WRITE_SIZE"].values())
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    out = {"copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_scale": fs, "write_scale": ws}
+    for k, src in KERNEL_SOURCES.items():
+        if k in fetch and k in write:
+            fk, wk = fetch[k]["FETCH_SIZE"], write[k]["WRITE_SIZE"]
+            out[k] = {"sources": src, "source_digest": source_digest(src), "dispatches": [nf[k], nw[k]],
+                      "fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(round(fk * 1024 * fs + wk * 1024 * ws))}
+    return out
+
+
 def trace_summary(path):
     """Per-kernel count, median, mean, min and max duration (us) of a rocprofv3 kernel-trace CSV."""
     import csv
@@ -232,10 +288,23 @@ def main():
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print per-kernel launch statistics (median, mean, min, max) of a rocprofv3 kernel "
                          "trace and exit (no GPU needed)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM bytes per launch from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration command, as JSON, and exit (no GPU needed)")
+    ap.add_argument("--counter-summary", metavar="COUNTER_CSV",
+                    help="print per-kernel mean counter values per dispatch of a rocprofv3 counter run and exit")
     args = ap.parse_args()
     if args.trace_summary:
         for r in trace_summary(args.trace_summary):
             print(json.dumps(r))
+        return
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(*args.traffic_summary), indent=1))
+        return
+    if args.counter_summary:
+        means, n = counter_means(args.counter_summary)
+        for k, d in means.items():
+            print(json.dumps({"kernel": k, "dispatches": n[k], **{c: round(v, 1) for c, v in sorted(d.items())}}))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -269,7 +338,7 @@ def main():
     sec_hot = time_launches(step, 1, args.steps, args.warmup, torch)
     value = flops / sec / 1e12
     log(f"bench: dense {sec * 1e6:.1f} us/launch ({sec_hot * 1e6:.1f} hot), {value:.1f} TFLOP/s")
-    traffic = traffic_for("attn_bf16_quad", 1)
+    traffic = traffic_for("attn_bf16_quad")
     result = {
         "metric": "attention TFLOP/s (% MFMA peak) dense; GB/s (% HBM peak) banded diff-attn",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -320,7 +389,8 @@ def main():
         outs = [torch.empty_like(s_[0]) for s_ in sets]
         kern = "xattn_bf16 (keys in LDS, one pass)" if wl.Sk <= 128 else "xattn_bf16 (keys in LDS, 64-key chunks)"
         form(name, wl, kern, lambda i: ka.ka_xattn_fwd(*sets[i], o=outs[i], scale=wl.scale), n, f, b,
-             "hbm" if f / b < acc.MFMA_BF16_PEAK / acc.HBM_PEAK else "mfma")
+             "hbm" if f / b < acc.MFMA_BF16_PEAK / acc.HBM_PEAK else "mfma",
+             **({"traffic": traffic_for("xattn_bf16")} if name == "cross" else {}))
         del sets, outs
     # ---------------- head dim 512: the SDXL VAE's single-head mid-block attention
     if "vae_mid" in wanted:
@@ -355,7 +425,7 @@ def main():
             def band(i):
                 ins, (a_, g_, b_, l_) = sets[i]
                 ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window)
-            form("band_diff", wl, "diff_band", band, len(sets), f, b, "hbm", traffic=traffic_for("diff_band", 1))
+            form("band_diff", wl, "diff_band", band, len(sets), f, b, "hbm", traffic=traffic_for("diff_band"))
         if "band_model" in wanted:
             def band_model(i):
                 ins, (a_, g_, b_, l_) = sets[i]
@@ -403,7 +473,9 @@ def main():
             def full(i):
                 ins, (a_, g_, b_, l_) = sets[i]
                 ka.ka_diffattn_fwd(*ins, a_, g_, b_, l_, o=outs[i], scale=wl.scale, window=wl.window, workspace=wss[i])
-            form("full_diff", wl, "diff_kprep + diff_flash_duo", full, len(sets), f, b, "mfma")
+            t1, t2 = traffic_for("diff_kprep"), traffic_for("diff_flash_duo")
+            form("full_diff", wl, "diff_kprep + diff_flash_duo", full, len(sets), f, b, "mfma",
+                 traffic=(t1 + t2) if t1 is not None and t2 is not None else None)
         if "full_model" in wanted:
             pad = 142
             w_, lm_ = (up(x, torch) for x in synth.make_model_params(wl.H, 1000 * wl.index + 6))

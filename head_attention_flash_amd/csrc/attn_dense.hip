@@ -116,8 +116,14 @@ __global__ __launch_bounds__(F32_BQ) void attn_f32_kernel(const float* __restric
 // LDS pitches (in 16-bit elements): K rows are read as 16-byte A-operand chunks,
 // V rows through the transposed 8-byte read; both pitches keep a wave's reads on
 // distinct banks.
-constexpr int KP = HD + 8;
-constexpr int VP = HD + 16;
+#ifndef DENSE_KPAD
+#define DENSE_KPAD 8
+#endif
+#ifndef DENSE_VPAD
+#define DENSE_VPAD 16
+#endif
+constexpr int KP = HD + DENSE_KPAD;
+constexpr int VP = HD + DENSE_VPAD;
 constexpr int BN = 64;  // keys per tile of the 16-query kernel
 
 // ---------------------------------------------------------------- bf16, 16 queries per wave, software-pipelined

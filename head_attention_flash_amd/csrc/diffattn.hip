@@ -202,7 +202,10 @@ __device__ __forceinline__ void load_pairs(const unsigned short* row, int d0, in
 // block computes.
 constexpr int BAND_BM = 64;  // query rows per block step: 4 waves x 16
 constexpr int BAND_NW = 4;
-constexpr int BAND_TARGET_WGS = 768;  // about three resident workgroups per CU
+#ifndef BAND_TARGET_WGS_SET
+#define BAND_TARGET_WGS_SET 768
+#endif
+constexpr int BAND_TARGET_WGS = BAND_TARGET_WGS_SET;  // about three resident workgroups per CU
 #ifndef BAND_WPE
 #define BAND_WPE 3
 #endif
