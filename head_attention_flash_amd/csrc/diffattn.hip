@@ -37,10 +37,10 @@
 //   diff_kprep         full (or wide-window) path, pass 1: DyT + rotation of K1 and
 //                      K2, once per (b, h) and key -- never once per query block
 //                      (V1 / Session 8: re-preparing K per query block was half the
-//                      kernel's vector work) -- into the fp16 workspace; with V
-//                      flags also V with the flagged-out rows zeroed.
-//   diff_flash_split   pass 2: eight waves per 64 queries, one branch per wave; q prep
-//                      in registers, then a pipelined flash loop over 64-key tiles of the
+//                      kernel's vector work) -- and V as fp16 (flagged-out rows
+//                      zeroed), into the workspace.
+//   diff_flash_duo     pass 2: four waves per 32 queries, one branch per wave; q prep
+//                      in registers, then a pipelined flash loop over 32-key tiles of the
 //                      prepared keys and V; branch 2 is subtracted through LDS at the end.
 #include <mutex>
 #include <type_traits>
@@ -190,6 +190,18 @@ __device__ __forceinline__ void load_pairs(const unsigned short* row, int d0, in
   }
   unpack_bf16x8(a, lo);
   unpack_bf16x8(b, hi);
+}
+
+// Workgroups that share a CU are issued oldest first, so with equal work per workgroup the
+// youngest one falls behind and finishes alone, on a CU it no longer fills.  A wave that has
+// more of its work left takes a higher priority (four levels by the fraction left), so the
+// waves of a CU advance together and finish together.
+__device__ __forceinline__ void priority_by_work_left(int left, int total) {
+  const int lv = (4 * left) / (total + 1);
+  if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
 }
 
 // ---------------------------------------------------------------- banded, strip-mined
@@ -397,6 +409,7 @@ void diff_band(DiffArgs a, int nblk, int nstrip) {
   for (int b = 0; b < nblk; ++b) {
     const int r0 = strip0 + b * BAND_BM;
     if (r0 >= S) break;
+    priority_by_work_left(nblk - b, nblk);
     const bool more = b + 1 < nblk && r0 + BAND_BM < S;
     // prepared queries of this block
     const int q0 = r0 + 16 * w, p = q0 + col;
@@ -583,29 +596,6 @@ void diff_flash_duo(DiffArgs a, int nqb) {
 
   const int qa = (item % nqb) * QWG, qb_ = min(S - 1, qa + QWG - 1);
   const int q0 = qa + QPW * wq;  // first query of this wave; block i holds q0 + 16 i + col
-  f16x8 Qf[NQB][2];
-  {
-    // this branch's queries (q1 with set 0, or q2 with set 2), requested before the parameters
-    // are staged so that the two latencies overlap
-    const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
-    const unsigned short* qt = br ? a.q2 : a.q1;
-    float lo[NQB][8], hi[NQB][8];
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      const int p = q0 + 16 * i + col;
-      const size_t pc = p < S ? p : 0;
-      load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo[i], hi[i]);
-    }
-    load_params<NORM>(sp, a);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NQB; ++i) {
-      prep_pairs2<NORM, RED_GROUP4, true>(lo[i], hi[i], lo[i], hi[i], qd0, gap, 8 * grp, q0 + 16 * i + col, set, set,
-                                          sp);
-      Qf[i][0] = to_f16x8(lo[i]);
-      Qf[i][1] = to_f16x8(hi[i]);
-    }
-  }
 
   int t_lo = 0, t_hi = (S - 1) / FBN;
   if (BAND) {
@@ -622,6 +612,39 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   // staging: thread tid moves row tid / 8, 16-byte column tid % 8 of each tensor's tile
   const int srow = tid >> 3, scol = (tid & 7) * 8;
   auto ld = [&](const rsrc_t& r, int u) { return buf_ld16(r, ((t_lo + u) * FBN + srow) * (HD * 2) + (tid & 7) * 16); };
+  uint4 k1t0, k2t0, k1t1, k2t1, stk1, stk2, stv;
+  f16x8 Qf[NQB][2];
+  {
+    // this branch's queries (q1 with set 0, or q2 with set 2), the parameters, and then the first
+    // two key tiles and the staged K(2) / V(0) are all requested before the first wait, so that
+    // the key loads overlap the query preparation
+    const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
+    const unsigned short* qt = br ? a.q2 : a.q1;
+    float lo[NQB][8], hi[NQB][8];
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      const int p = q0 + 16 * i + col;
+      const size_t pc = p < S ? p : 0;
+      load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo[i], hi[i]);
+    }
+    load_params<NORM>(sp, a);
+    k1t0 = ld(k1rs, 0);
+    k2t0 = ld(k2rs, 0);
+    k1t1 = ld(k1rs, 1);  // past the last tile: zeros
+    k2t1 = ld(k2rs, 1);
+    stk1 = ld(k1rs, 2);
+    stk2 = ld(k2rs, 2);
+    stv = ld(vrs, 0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NQB; ++i) {
+      prep_pairs2<NORM, RED_GROUP4, true>(lo[i], hi[i], lo[i], hi[i], qd0, gap, 8 * grp, q0 + 16 * i + col, set, set,
+                                          sp);
+      Qf[i][0] = to_f16x8(lo[i]);
+      Qf[i][1] = to_f16x8(hi[i]);
+    }
+  }
+
   const unsigned short(*Kr)[FBN * KPD] = br ? sm.K2 : sm.K1;  // this wave's branch keys
 
   f32x4 O[4][NQB], L[NQB];
@@ -638,11 +661,13 @@ void diff_flash_duo(DiffArgs a, int nqb) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
-  uint4 stk1, stk2, stv;
   f32x4 Sa[2][NQB], Sb[2][NQB];
-  // prologue: K(0) -> ring 0, S(0) = K(0) Q^T; K(1) -> ring 1; stage K(2) and V(0)
-  st16(&sm.K1[0][srow * KPD + scol], ld(k1rs, 0));
-  st16(&sm.K2[0][srow * KPD + scol], ld(k2rs, 0));
+  // prologue: K(0) -> ring 0, K(1) -> ring 1 (a tile past the last is never read), then
+  // S(0) = K(0) Q^T; K(2) and V(0) stay staged in registers
+  st16(&sm.K1[0][srow * KPD + scol], k1t0);
+  st16(&sm.K2[0][srow * KPD + scol], k2t0);
+  st16(&sm.K1[1][srow * KPD + scol], k1t1);
+  st16(&sm.K2[1][srow * KPD + scol], k2t1);
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -654,19 +679,13 @@ void diff_flash_duo(DiffArgs a, int nqb) {
       Sa[kb][i] = mfma_f16(a1, Qf[i][1], Sa[kb][i]);
     }
   }
-  if (T > 1) {
-    st16(&sm.K1[1][srow * KPD + scol], ld(k1rs, 1));
-    st16(&sm.K2[1][srow * KPD + scol], ld(k2rs, 1));
-  }
-  stk1 = ld(k1rs, 2);  // past the last tile: zeros, never stored
-  stk2 = ld(k2rs, 2);
-  stv = ld(vrs, 0);
-  __syncthreads();
+  __syncthreads();  // ring 0 is rewritten in step 0
 
   auto step = [&](auto has_next, auto has_prev, auto parity, int t, f32x4 (&Sc)[2][NQB], f32x4 (&Sn)[2][NQB]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
     constexpr int PAR = decltype(parity)::value;  // t & 1
+    if ((t & 3) == 0) priority_by_work_left(T - t, T);
     f16x8 kf[2][2], vf[4];
     if (NEXT) {
       const unsigned short* Kt = Kr[PAR ^ 1];
