@@ -176,9 +176,13 @@ def test_dense_layouts_agree(Sq):
     assert dmax <= BF16_TOL
 
 
-def test_dense_bf16_deterministic():
+@pytest.mark.parametrize("shape", [(1, 3, 1000, 900), None])
+def test_dense_bf16_deterministic(shape):
+    """Repeated calls give the same bits (no atomics, no order-dependent reductions), also at the
+    workload's size, where two blocks share each CU."""
     wl = W["sdxl_l1_self_b2h10s4096"]
-    q, k, v = (to_dev(x) for x in synth.make_dense(wl, B=1, H=3, Sq=1000, Sk=900))
+    kw = {} if shape is None else dict(zip(("B", "H", "Sq", "Sk"), shape))
+    q, k, v = (to_dev(x) for x in synth.make_dense(wl, **kw))
     a = ka.ka_attn_fwd(q, k, v)
     b = ka.ka_attn_fwd(q, k, v)
     torch.cuda.synchronize()
@@ -313,11 +317,16 @@ def test_diff_constant_v(window):
     assert_close(got, np.broadcast_to(want, got.shape), 1e-2, f"constant V w={window}")
 
 
-def test_diff_deterministic():
-    wl = W["sa3_decoder_banddiff_h8s23086w17"]
-    inputs, params = synth.make_diff(wl, seed_base=920, S=1000, H=2)
-    a = _run_diff(inputs, params, 17)
-    b = _run_diff(inputs, params, 17)
+@pytest.mark.parametrize("key,small", [("sa3_decoder_banddiff_h8s23086w17", True),
+                                       ("sa3_decoder_banddiff_h8s23086w17", False),
+                                       ("sa3_dit_fulldiff_h16s1422", False)])
+def test_diff_deterministic(key, small):
+    """Repeated calls give the same bits, also at the workloads' sizes, where several workgroups
+    share each CU (and set their wave priorities by the work they have left)."""
+    wl = W[key]
+    inputs, params = synth.make_diff(wl, seed_base=920, **(dict(S=1000, H=2) if small else {}))
+    a = _run_diff(inputs, params, wl.window, bits=True)[1]
+    b = _run_diff(inputs, params, wl.window, bits=True)[1]
     assert np.array_equal(a, b)
 
 
