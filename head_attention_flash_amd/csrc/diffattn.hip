@@ -503,7 +503,8 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
 //   * issues the matrix work of S(t+1) = K(t+1) Q^T and of O += V(t-1)^T P(t-1)^T,
 //   * forms the weights of tile t on the vector unit, one weight beside each MFMA, the order
 //     fixed by scheduling barriers,
-//   * stores the staged K1/K2(t+2) and V(t) into the ring slots read last in step t - 1,
+//   * requests K1/K2(t+2) and V(t) straight into the ring slots read last before the previous
+//     barrier (buffer loads into LDS, no staging registers), waiting for them before its barrier,
 // then the block synchronises once.  Weights are 2^(c s - R) with R at the query's running
 // maximum (in the exp2 domain), so they stay below 2^F_LAZY until a score passes the maximum
 // by F_LAZY: a packed 16-bit maximum over the fp16 weights and a wave-wide vote replace the
@@ -523,12 +524,8 @@ constexpr int FBN = 32;      // keys per tile
 #ifndef F_VLEAD_SET
 #define F_VLEAD_SET 1
 #endif
-#ifndef F_STG_SET
-#define F_STG_SET 4
-#endif
 constexpr int F_VSLOT = F_VSLOT_SET;  // MFMA slot after which a step reads its V fragments
 constexpr int F_VLEAD = F_VLEAD_SET;  // vector work runs this many slots ahead of the MFMAs
-constexpr int F_STG = F_STG_SET;      // vector slot at which the staged tiles are stored
 // One 16-query block per wave (32 queries per workgroup: 720 workgroups for 16 heads x 1422
 // tokens, 2.8 per CU) measured faster than two (368 workgroups: 49.5 vs 42.5 us for both passes):
 // the finer grid balances the chip better than the longer steps amortise their latency.
@@ -560,11 +557,44 @@ __device__ __forceinline__ int xcd_major(int blk, int n) {
   return blk < n8 ? (blk & 7) * (n8 >> 3) + (blk >> 3) : blk;
 }
 
+// The rings hold unpadded 128-byte rows whose 16-byte chunks are XOR-swizzled by row, so that the
+// fragment reads below hit distinct banks: chunk c of row r sits at chunk position c ^ swz(r).
 struct FullLds {
-  unsigned short K1[2][FBN * KPD];
-  unsigned short K2[2][FBN * KPD];
-  unsigned short V[2][FBN * VPD];
+  unsigned short K1[2][FBN * HD];
+  unsigned short K2[2][FBN * HD];
+  unsigned short V[2][FBN * HD];
 };
+// K: a b128 fragment read takes one chunk of 16 consecutive rows; rows 2m, 2m + 1 share a
+// position and fall in the two 128-byte halves of the banks, the 8 pairs in 8 positions.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+// V: the transposed reads take 8-byte halves of one chunk from rows 4 apart.
+__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
+
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+// The four words of a raw buffer descriptor (the format make_rsrc builds), in scalar registers.
+__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
+  r[3] = RSRC_FLAGS;
+  return r;
+}
+// 16 bytes per lane from the buffer (offsets past its size read as zero) straight into LDS, lane l's
+// bytes at lds_base + 16 l.  M0 carries the wave's LDS base and is restored afterwards.  Inline
+// assembly, so that the compiler does not make every later LDS read wait for the load: the caller
+// waits (s_waitcnt) right before the barrier that publishes the data.
+__device__ __forceinline__ void load16_to_lds(u32x4_t rsrc, int voff, unsigned lds_base) {
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const unsigned short*)p);
+}
 
 template <bool BAND, int NORM, int NQB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FULL_WPE, FULL_WPE)))
@@ -572,7 +602,7 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   constexpr int QPW = 16 * NQB;    // queries of a wave
   constexpr int QWG = 2 * QPW;     // queries of a block (two waves per branch)
   static_assert(FBN * 8 == 256, "one 16-byte chunk of each tensor per thread and tile");
-  static_assert(2 * 2 * FBN * KPD * 2 >= 2 * NQB * 4 * 64 * 16, "the branch-2 hand-over must fit the K rings");
+  static_assert(2 * 2 * FBN * HD * 2 >= 2 * NQB * 4 * 64 * 16, "the branch-2 hand-over must fit the K rings");
   __shared__ __align__(16) FullLds sm;
   __shared__ SharedParams sp;
 
@@ -607,17 +637,26 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   const _Float16* k1h = a.ws + base;
   const _Float16* k2h = a.ws + nrows * HD + base;
   const _Float16* vh = a.ws + 2 * nrows * HD + base;
-  // rows past S read as zero through the buffer resources
-  const rsrc_t k1rs = make_rsrc(k1h, rbytes), k2rs = make_rsrc(k2h, rbytes), vrs = make_rsrc(vh, rbytes);
-  // staging: thread tid moves row tid / 8, 16-byte column tid % 8 of each tensor's tile
-  const int srow = tid >> 3, scol = (tid & 7) * 8;
-  auto ld = [&](const rsrc_t& r, int u) { return buf_ld16(r, ((t_lo + u) * FBN + srow) * (HD * 2) + (tid & 7) * 16); };
-  uint4 k1t0, k2t0, k1t1, k2t1, stk1, stk2, stv;
+  // rows past S read as zero through the descriptors
+  const u32x4_t k1rs = raw_rsrc(k1h, rbytes), k2rs = raw_rsrc(k2h, rbytes), vrs = raw_rsrc(vh, rbytes);
+  // tile u of a tensor into a ring slot: wave w moves rows 8 w .. 8 w + 7 in one instruction, lane l
+  // the chunk of row 8 w + l / 8 that belongs at chunk position l % 8
+  const int drow = 8 * w + (lane >> 3), dpos = lane & 7;
+  const int doff_k = drow * (HD * 2) + ((dpos ^ swz_k(drow)) << 4);
+  const int doff_v = drow * (HD * 2) + ((dpos ^ swz_v(drow)) << 4);
+  auto dma = [&](const u32x4_t& r, int doff, int u, const unsigned short* slot) {
+    load16_to_lds(r, (t_lo + u) * (FBN * HD * 2) + doff, lds_addr(slot + 8 * w * HD));
+  };
+  // the first two key tiles, requested before anything else so that their latency overlaps the
+  // query loads and the query preparation
+  dma(k1rs, doff_k, 0, sm.K1[0]);
+  dma(k2rs, doff_k, 0, sm.K2[0]);
+  dma(k1rs, doff_k, 1, sm.K1[1]);  // past the last tile: zeros, never read
+  dma(k2rs, doff_k, 1, sm.K2[1]);
   f16x8 Qf[NQB][2];
   {
-    // this branch's queries (q1 with set 0, or q2 with set 2), the parameters, and then the first
-    // two key tiles and the staged K(2) / V(0) are all requested before the first wait, so that
-    // the key loads overlap the query preparation
+    // this branch's queries (q1 with set 0, or q2 with set 2), requested before the parameters are
+    // staged so that the two latencies overlap
     const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
     const unsigned short* qt = br ? a.q2 : a.q1;
     float lo[NQB][8], hi[NQB][8];
@@ -628,13 +667,6 @@ void diff_flash_duo(DiffArgs a, int nqb) {
       load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo[i], hi[i]);
     }
     load_params<NORM>(sp, a);
-    k1t0 = ld(k1rs, 0);
-    k2t0 = ld(k2rs, 0);
-    k1t1 = ld(k1rs, 1);  // past the last tile: zeros
-    k2t1 = ld(k2rs, 1);
-    stk1 = ld(k1rs, 2);
-    stk2 = ld(k2rs, 2);
-    stv = ld(vrs, 0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
@@ -645,7 +677,7 @@ void diff_flash_duo(DiffArgs a, int nqb) {
     }
   }
 
-  const unsigned short(*Kr)[FBN * KPD] = br ? sm.K2 : sm.K1;  // this wave's branch keys
+  const unsigned short(*Kr)[FBN * HD] = br ? sm.K2 : sm.K1;  // this wave's branch keys
 
   f32x4 O[4][NQB], L[NQB];
   float R[NQB];
@@ -662,17 +694,25 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
   f32x4 Sa[2][NQB], Sb[2][NQB];
-  // prologue: K(0) -> ring 0, K(1) -> ring 1 (a tile past the last is never read), then
-  // S(0) = K(0) Q^T; K(2) and V(0) stay staged in registers
-  st16(&sm.K1[0][srow * KPD + scol], k1t0);
-  st16(&sm.K2[0][srow * KPD + scol], k2t0);
-  st16(&sm.K1[1][srow * KPD + scol], k1t1);
-  st16(&sm.K2[1][srow * KPD + scol], k2t1);
+  // K fragment (A operand) of 16-key block kb, dims 32 hh + 8 grp .. + 8
+  auto kfrag = [&](const unsigned short* Kt, int kb, int hh) {
+    const int r = 16 * kb + col;
+    return *reinterpret_cast<const f16x8*>(&Kt[r * HD + (((4 * hh + grp) ^ swz_k(r)) << 3)]);
+  };
+  // V^T fragment (A operand) of dims 16 db .. + 16: lane row = head dim, k = key in the order of the
+  // P^T operand (keys 4 grp + e of the first 16-key half, then of the second)
+  auto vfrag = [&](const unsigned short* Vt, int db) {
+    const int r0 = 4 * grp + (col >> 2), r1 = r0 + 16, ch = 2 * db + ((col & 3) >> 1), half = 4 * (col & 1);
+    return cat_f16(lds_read_tr16(&Vt[r0 * HD + ((ch ^ swz_v(r0)) << 3) + half]),
+                   lds_read_tr16(&Vt[r1 * HD + ((ch ^ swz_v(r1)) << 3) + half]));
+  };
+  // prologue: K(0) and K(1) have landed in rings 0 and 1 (a tile past the last is never read); then
+  // S(0) = K(0) Q^T
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kr[0][(16 * kb + col) * KPD + 8 * grp]);
-    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kr[0][(16 * kb + col) * KPD + 32 + 8 * grp]);
+    const f16x8 a0 = kfrag(Kr[0], kb, 0), a1 = kfrag(Kr[0], kb, 1);
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
       Sa[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -686,14 +726,20 @@ void diff_flash_duo(DiffArgs a, int nqb) {
     constexpr bool PREV = decltype(has_prev)::value;
     constexpr int PAR = decltype(parity)::value;  // t & 1
     if ((t & 3) == 0) priority_by_work_left(T - t, T);
+    // K1 / K2 (t + 2) and V(t) go straight into the ring slots read last before the previous barrier
+    // (K(t) for S(t), V(t - 2) for the P.V of step t - 1); they are waited for before this step's
+    // barrier
+    if (t + 2 < T) {
+      dma(k1rs, doff_k, t + 2, sm.K1[PAR]);
+      dma(k2rs, doff_k, t + 2, sm.K2[PAR]);
+    }
+    dma(vrs, doff_v, t, sm.V[PAR]);
     f16x8 kf[2][2], vf[4];
     if (NEXT) {
-      const unsigned short* Kt = Kr[PAR ^ 1];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          kf[kb][hh] = *reinterpret_cast<const f16x8*>(&Kt[(16 * kb + col) * KPD + 32 * hh + 8 * grp]);
+        for (int hh = 0; hh < 2; ++hh) kf[kb][hh] = kfrag(Kr[PAR ^ 1], kb, hh);
     }
     // V fragments are read right after MFMA slot VS, before the first P.V product (slot NQK);
     // steps without QK work start their P.V products at slot 0 and read them up front
@@ -702,12 +748,8 @@ void diff_flash_duo(DiffArgs a, int nqb) {
     auto load_v = [&]() {
       // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
       const unsigned short* Vt = sm.V[PAR ^ 1];
-      const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int vcol = 16 * db + 4 * (col & 3);
-        vf[db] = cat_f16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
-      }
+      for (int db = 0; db < 4; ++db) vf[db] = vfrag(Vt, db);
     };
     if (PREV && VS < 0) load_v();
     // keys past S (last tile) or outside the band of some query of the block take no weight
@@ -774,17 +816,6 @@ void diff_flash_duo(DiffArgs a, int nqb) {
         constexpr int SM = SL - F_VLEAD;
         if constexpr (SM >= 0) mfma_at(std::integral_constant<int, SM>{});
         if constexpr (PREV && VS >= 0 && SM == VS) load_v();
-        if constexpr (SL == (F_STG < NSLOT ? F_STG : NSLOT - 1)) {
-          // the ring slots written here were last read in step t - 1
-          if (t + 2 < T) {
-            st16(&sm.K1[PAR][srow * KPD + scol], stk1);
-            st16(&sm.K2[PAR][srow * KPD + scol], stk2);
-          }
-          st16(&sm.V[PAR][srow * VPD + scol], stv);
-          stk1 = ld(k1rs, t + 3);  // past the last tile: zeros, never stored
-          stk2 = ld(k2rs, t + 3);
-          stv = ld(vrs, t + 1);
-        }
         valu_at(std::integral_constant<int, SL>{});
         __builtin_amdgcn_sched_barrier(0);
       }(), ...);
@@ -814,6 +845,7 @@ void diff_flash_duo(DiffArgs a, int nqb) {
     }
 #pragma unroll
     for (int i = 0; i < NQB; ++i) P[i] = __builtin_bit_cast(f16x8, make_uint4(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]));
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tiles have landed
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
@@ -838,11 +870,9 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   }
   {  // P.V of the last tile
     const unsigned short* Vt = sm.V[(T - 1) & 1];
-    const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const f16x8 av = cat_f16(lds_read_tr16(&Vt[vrow * VPD + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VPD + vcol]));
+      const f16x8 av = vfrag(Vt, db);
 #pragma unroll
       for (int i = 0; i < NQB; ++i) O[db][i] = mfma_f16(av, P[i], O[db][i]);
     }
