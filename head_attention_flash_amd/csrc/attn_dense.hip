@@ -393,9 +393,10 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 //   * issues the matrix work of S(t+1) = K(t+1) Q^T and of O += V(t-1)^T P(t-1)^T,
 //   * computes the weights of tile t on the vector unit, one weight (or one bf16
 //     pack) beside each MFMA, the instruction order fixed by scheduling barriers,
-//   * stores the staged K(t+2) / V(t) into the ring slots read last in step t-1,
-// then the block synchronises once.  Threads 0-255 stage K, 256-511 stage V, one
-// 16-byte chunk each per tile, loaded one step before it is stored.
+//   * requests K(t+2) / V(t) straight into the ring slots read last before the previous
+//     barrier (buffer loads into LDS: no staging registers, no LDS stores; each wave moves
+//     8 rows of a tile and waits for them right before the barrier),
+// then the block synchronises once.  Waves 0-3 move K, waves 4-7 move V.
 //
 // Vector work is what bounds this loop on CDNA4 (an MFMA hides little of it), so a
 // weight takes one FMA and one v_exp and nothing else but the bf16 pack:
@@ -410,11 +411,11 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
 constexpr int DBN = 32;       // keys per tile
 constexpr int DUO_VSLOT = 5;  // MFMA slot at which a step reads its V fragments
 constexpr int DUO_VLEAD = 1;  // vector work runs this many slots ahead of the MFMAs
-constexpr int DUO_STG = 4;    // 4-wave form: vector slot at which the staged K / V are stored
 
+// unpadded 128-byte rows, 16-byte chunks XOR-swizzled by row (swz_k, swz_v)
 struct DuoLds {
-  unsigned short K[2][DBN * KP];
-  unsigned short V[2][DBN * VP];
+  unsigned short K[2][DBN * HD];
+  unsigned short V[2][DBN * HD];
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -425,27 +426,40 @@ __device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// QUAD = false: 512-thread block, threads 0-255 stage K and 256-511 stage V, each tile
-// loaded one step before it is stored (two staging registers).  QUAD = true: 256-thread
-// block, every thread stages one K and one V chunk per tile, loaded right after the
-// previous store so that one staging register per stream suffices.
+// QUAD = false: 512-thread block, waves 0-3 move the K tiles and waves 4-7 the V tiles.  QUAD =
+// true: 256-thread block, every wave moves 8 rows of each K and V tile.
 template <int NQB, bool QUAD>
 __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __restrict__ qb, int Sq, int q0,
                                          const unsigned short* kbase, const unsigned short* vbase, int Sk, float c,
                                          unsigned short* __restrict__ ob, int tid) {
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const bool isK = QUAD || __builtin_amdgcn_readfirstlane(tid >> 6) < 4;  // wave-uniform: a scalar buffer resource
-  const int chunk = tid & 255, srow = chunk >> 3, scol = (chunk & 7) * 8;
-  // rows past Sk read as zero through the buffer resource
-  const rsrc_t srs = make_rsrc(isK ? kbase : vbase, Sk * HD * 2);
-  const rsrc_t vrs = make_rsrc(vbase, Sk * HD * 2);
-  const int lead = isK ? 2 : 0;  // step t stores tile t + lead and loads tile t + lead + 1
-  unsigned short* sdst0 = isK ? &sm.K[0][srow * KP + scol] : &sm.V[0][srow * VP + scol];
-  unsigned short* sdst1 = isK ? &sm.K[1][srow * KP + scol] : &sm.V[1][srow * VP + scol];
-  unsigned short* vdst0 = &sm.V[0][srow * VP + scol];
-  unsigned short* vdst1 = &sm.V[1][srow * VP + scol];
-  auto ldt = [&](int tile) { return buf_ld16(srs, tile * (DBN * HD * 2) + chunk * 16); };
-  auto ldv = [&](int tile) { return buf_ld16(vrs, tile * (DBN * HD * 2) + chunk * 16); };
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool isK = QUAD || w < 4;  // the 8-wave form: waves 0-3 move K, 4-7 move V
+  // rows past Sk read as zero through the descriptors
+  const u32x4_t krs = raw_rsrc(kbase, Sk * HD * 2), vrs = raw_rsrc(vbase, Sk * HD * 2);
+  // a tile into a ring slot: wave w (of the four that move a tensor) moves rows 8 (w % 4) .. + 7 in
+  // one instruction, lane l the chunk of row 8 (w % 4) + l / 8 that belongs at chunk position l % 8
+  const int wl = w & 3, drow = 8 * wl + (lane >> 3), dpos = lane & 7;
+  const int doff_k = drow * (HD * 2) + ((dpos ^ swz_k(drow)) << 4);
+  const int doff_v = drow * (HD * 2) + ((dpos ^ swz_v(drow)) << 4);
+  auto dma_k = [&](int tile, int slot) {
+    load16_to_lds(krs, tile * (DBN * HD * 2) + doff_k, lds_addr(&sm.K[slot][8 * wl * HD]));
+  };
+  auto dma_v = [&](int tile, int slot) {
+    load16_to_lds(vrs, tile * (DBN * HD * 2) + doff_v, lds_addr(&sm.V[slot][8 * wl * HD]));
+  };
+  // K fragment (A operand) of 16-key block kb, dims 32 h + 8 grp .. + 8
+  auto kfrag = [&](const unsigned short* Kt, int kb, int h) {
+    const int r = 16 * kb + col;
+    return *reinterpret_cast<const bf16x8*>(&Kt[r * HD + (((4 * h + grp) ^ swz_k(r)) << 3)]);
+  };
+  // V^T fragment (A operand) of dims 16 db .. + 16: lane row = head dim, k = key in the order of the
+  // P^T operand (keys 4 grp + e of the first 16-key half, then of the second)
+  auto vfrag = [&](const unsigned short* Vt, int db) {
+    const int r0 = 4 * grp + (col >> 2), r1 = r0 + 16, ch = 2 * db + ((col & 3) >> 1), half = 4 * (col & 1);
+    return cat_bf16(lds_read_tr16(&Vt[r0 * HD + ((ch ^ swz_v(r0)) << 3) + half]),
+                    lds_read_tr16(&Vt[r1 * HD + ((ch ^ swz_v(r1)) << 3) + half]));
+  };
 
   bf16x8 Qf[NQB][2];
 #pragma unroll
@@ -475,39 +489,39 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   const int T = (Sk + DBN - 1) / DBN;
-  uint4 st[2], stv;
   f32x4 Sa[2][NQB], Sb[2][NQB];
-  // prologue: K(0) -> K[0], S(0) = K(0) Q^T; K(1) -> K[1]; stage K(2) / V(0)
-  if (isK) st16(sdst0, ldt(0));
+  // prologue: K(0) -> K[0] and K(1) -> K[1] (a tile past the last is never read), then S(0) = K(0) Q^T
+  if (isK) {
+    dma_k(0, 0);
+    dma_k(1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sm.K[0][(16 * kb + col) * KP + 8 * grp]);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sm.K[0][(16 * kb + col) * KP + 32 + 8 * grp]);
+    const bf16x8 a0 = kfrag(sm.K[0], kb, 0), a1 = kfrag(sm.K[0], kb, 1);
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
       Sa[kb][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qf[i][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       Sa[kb][i] = mfma_bf16(a1, Qf[i][1], Sa[kb][i]);
     }
   }
-  if (isK && T > 1) st16(sdst1, ldt(1));
-  st[0] = ldt(lead);
-  if constexpr (QUAD) stv = ldv(0);
-  __syncthreads();
+  __syncthreads();  // K[0] is rewritten in step 0
 
   auto step = [&](auto has_next, auto has_prev, auto parity, int t, f32x4 (&Sc)[2][NQB], f32x4 (&Sn)[2][NQB]) {
     constexpr bool NEXT = decltype(has_next)::value;
     constexpr bool PREV = decltype(has_prev)::value;
     constexpr int PAR = decltype(parity)::value;  // t & 1
-    if constexpr (!QUAD) st[PAR ^ 1] = ldt(t + lead + 1);  // past the last tile: zeros, never stored
+    // K(t+2) and V(t) go straight into the ring slots read last before the previous barrier (K(t) for
+    // S(t), V(t-2) for the P.V of step t-1); each wave waits for its own before this step's barrier
+    if (isK && t + 2 < T) dma_k(t + 2, PAR);
+    if (QUAD || !isK) dma_v(t, PAR);
     bf16x8 kf[2][2], vf[4];
     if (NEXT) {
-      const unsigned short* Kt = sm.K[PAR ^ 1];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          kf[kb][h] = *reinterpret_cast<const bf16x8*>(&Kt[(16 * kb + col) * KP + 32 * h + 8 * grp]);
+        for (int h = 0; h < 2; ++h) kf[kb][h] = kfrag(sm.K[PAR ^ 1], kb, h);
     }
     // V fragments are read at MFMA slot DUO_VSLOT, after the K fragments have been consumed by the first
     // QK products; steps without QK work start their P.V products at slot 0 and read them up front
@@ -516,12 +530,8 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
       // V^T A operand: lane row = head dim, k = key in the order of the P^T operand
       // (keys 4*grp + e of the first 16-key half, then of the second)
       const unsigned short* Vt = sm.V[PAR ^ 1];
-      const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int vcol = 16 * db + 4 * (col & 3);
-        vf[db] = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
-      }
+      for (int db = 0; db < 4; ++db) vf[db] = vfrag(Vt, db);
     };
     if (PREV && VS < 0) load_v();
     if (!NEXT) {  // last tile: keys past Sk take no weight
@@ -582,13 +592,6 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
         constexpr int SM = S - DUO_VLEAD;
         if constexpr (SM >= 0) mfma_at(std::integral_constant<int, SM>{});
         if constexpr (PREV && VS >= 0 && SM == VS) load_v();
-        if constexpr (QUAD && S == (DUO_STG < NSLOT ? DUO_STG : NSLOT - 1)) {
-          // the ring slots written here were last read in step t - 1
-          if (t + 2 < T) st16(PAR ? sdst1 : sdst0, st[0]);
-          st16(PAR ? vdst1 : vdst0, stv);
-          st[0] = ldt(t + 3);  // past the last tile: zeros, never stored
-          stv = ldv(t + 1);
-        }
         valu_at(std::integral_constant<int, S>{});
         __builtin_amdgcn_sched_barrier(0);
       }(), ...);
@@ -621,9 +624,7 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
     }
 #pragma unroll
     for (int i = 0; i < NQB; ++i) P[i] = __builtin_bit_cast(bf16x8, make_uint4(Pw[i][0], Pw[i][1], Pw[i][2], Pw[i][3]));
-    if constexpr (!QUAD) {
-      if (t + lead < T) st16(PAR ? sdst1 : sdst0, st[PAR]);
-    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tiles have landed
     __syncthreads();
   };
   using yes = std::integral_constant<bool, true>;
@@ -648,11 +649,9 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   }
   {  // P.V of the last tile
     const unsigned short* Vt = sm.V[(T - 1) & 1];
-    const int vrow = 4 * grp + (col >> 2);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 a = cat_bf16(lds_read_tr16(&Vt[vrow * VP + vcol]), lds_read_tr16(&Vt[(vrow + 16) * VP + vcol]));
+      const bf16x8 a = vfrag(Vt, db);
 #pragma unroll
       for (int i = 0; i < NQB; ++i) O[db][i] = mfma_bf16(a, P[i], O[db][i]);
     }

@@ -564,38 +564,6 @@ struct FullLds {
   unsigned short K2[2][FBN * HD];
   unsigned short V[2][FBN * HD];
 };
-// K: a b128 fragment read takes one chunk of 16 consecutive rows; rows 2m, 2m + 1 share a
-// position and fall in the two 128-byte halves of the banks, the 8 pairs in 8 positions.
-__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
-// V: the transposed reads take 8-byte halves of one chunk from rows 4 apart.
-__device__ __forceinline__ int swz_v(int r) { return ((r >> 1) & 3) << 1; }
-
-typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
-// The four words of a raw buffer descriptor (the format make_rsrc builds), in scalar registers.
-__device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
-  const unsigned long long p = (unsigned long long)base;
-  u32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
-  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
-  r[2] = __builtin_amdgcn_readfirstlane((unsigned)bytes);
-  r[3] = RSRC_FLAGS;
-  return r;
-}
-// 16 bytes per lane from the buffer (offsets past its size read as zero) straight into LDS, lane l's
-// bytes at lds_base + 16 l.  M0 carries the wave's LDS base and is restored afterwards.  Inline
-// assembly, so that the compiler does not make every later LDS read wait for the load: the caller
-// waits (s_waitcnt) right before the barrier that publishes the data.
-__device__ __forceinline__ void load16_to_lds(u32x4_t rsrc, int voff, unsigned lds_base) {
-  unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory");
-}
-__device__ __forceinline__ unsigned lds_addr(const unsigned short* p) {
-  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) const unsigned short*)p);
-}
-
 template <bool BAND, int NORM, int NQB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FULL_WPE, FULL_WPE)))
 void diff_flash_duo(DiffArgs a, int nqb) {
