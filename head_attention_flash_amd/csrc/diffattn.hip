@@ -282,13 +282,16 @@ __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsi
                                             const f16x8 (&Qf)[2], const bool (&band)[NKB][4], bool edge, int jbase,
                                             int S, float c, int col, int grp, const bf16x8& ones, f32x4 (&O)[4],
                                             float& l) {
+  // s0 and NR are multiples of 16, so a ring wrap falls between 16-row groups: the wrapped group
+  // start is wave-uniform and the lane adds its row within the group
   f32x4 Sc[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    int s = s0 + 16 * kb + col;
-    s = s >= NR ? s - NR : s;
-    const f16x8 a0 = *reinterpret_cast<const f16x8*>(&Kh[s * KPD + 8 * grp]);
-    const f16x8 a1 = *reinterpret_cast<const f16x8*>(&Kh[s * KPD + 32 + 8 * grp]);
+    int sb = s0 + 16 * kb;
+    sb = sb >= NR ? sb - NR : sb;
+    const unsigned short* kr = Kh + sb * KPD + col * KPD + 8 * grp;
+    const f16x8 a0 = *reinterpret_cast<const f16x8*>(kr);
+    const f16x8 a1 = *reinterpret_cast<const f16x8*>(kr + 32);
     Sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     Sc[kb] = mfma_f16(a1, Qf[1], Sc[kb]);
   }
@@ -322,14 +325,14 @@ __device__ __forceinline__ void band_branch(const unsigned short* Kh, const unsi
 #pragma unroll
   for (int ks = 0; ks < NKB / 2; ++ks) {
     const bf16x8 P = pack_bf16(Sc[2 * ks], Sc[2 * ks + 1]);
-    int r = s0 + 32 * ks + 4 * grp + (col >> 2);
-    r = r >= NR ? r - NR : r;
-    int r16 = r + 16;
-    r16 = r16 >= NR ? r16 - NR : r16;
+    int rb = s0 + 32 * ks;
+    rb = rb >= NR ? rb - NR : rb;
+    int rb16 = rb + 16;
+    rb16 = rb16 >= NR ? rb16 - NR : rb16;
+    const int lv = (4 * grp + (col >> 2)) * VPD + 4 * (col & 3);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const int vcol = 16 * db + 4 * (col & 3);
-      const bf16x8 av = cat_bf16(lds_read_tr16(&Vs[r * VPD + vcol]), lds_read_tr16(&Vs[r16 * VPD + vcol]));
+      const bf16x8 av = cat_bf16(lds_read_tr16(&Vs[rb * VPD + lv + 16 * db]), lds_read_tr16(&Vs[rb16 * VPD + lv + 16 * db]));
       O[db] = mfma_bf16(av, P, O[db]);
     }
     L = mfma_bf16(ones, P, L);
