@@ -442,11 +442,14 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   const int wl = w & 3, drow = 8 * wl + (lane >> 3), dpos = lane & 7;
   const int doff_k = drow * (HD * 2) + ((dpos ^ swz_k(drow)) << 4);
   const int doff_v = drow * (HD * 2) + ((dpos ^ swz_v(drow)) << 4);
+  // the tile offset goes into the descriptor and the ring slot into M0, both scalar
+  constexpr unsigned SLOT = DBN * HD * 2;  // bytes of a ring slot
+  const unsigned lds_k = lds_addr(&sm.K[0][8 * wl * HD]), lds_v = lds_addr(&sm.V[0][8 * wl * HD]);
   auto dma_k = [&](int tile, int slot) {
-    load16_to_lds(krs, tile * (DBN * HD * 2) + doff_k, lds_addr(&sm.K[slot][8 * wl * HD]));
+    load16_to_lds(rsrc_advance(krs, (unsigned)tile * SLOT), doff_k, lds_k + slot * SLOT);
   };
   auto dma_v = [&](int tile, int slot) {
-    load16_to_lds(vrs, tile * (DBN * HD * 2) + doff_v, lds_addr(&sm.V[slot][8 * wl * HD]));
+    load16_to_lds(rsrc_advance(vrs, (unsigned)tile * SLOT), doff_v, lds_v + slot * SLOT);
   };
   // K fragment (A operand) of 16-key block kb, dims 32 h + 8 grp .. + 8
   auto kfrag = [&](const unsigned short* Kt, int kb, int h) {

@@ -612,18 +612,24 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   const u32x4_t k1rs = raw_rsrc(k1h, rbytes), k2rs = raw_rsrc(k2h, rbytes), vrs = raw_rsrc(vh, rbytes);
   // tile u of a tensor into a ring slot: wave w moves rows 8 w .. 8 w + 7 in one instruction, lane l
   // the chunk of row 8 w + l / 8 that belongs at chunk position l % 8
+  // The tile offset goes into the descriptor and the ring slot into M0, both scalar; the lane's
+  // part of the address is fixed.
   const int drow = 8 * w + (lane >> 3), dpos = lane & 7;
   const int doff_k = drow * (HD * 2) + ((dpos ^ swz_k(drow)) << 4);
   const int doff_v = drow * (HD * 2) + ((dpos ^ swz_v(drow)) << 4);
-  auto dma = [&](const u32x4_t& r, int doff, int u, const unsigned short* slot) {
-    load16_to_lds(r, (t_lo + u) * (FBN * HD * 2) + doff, lds_addr(slot + 8 * w * HD));
+  constexpr unsigned SLOT = FBN * HD * 2;  // bytes of a ring slot; FullLds holds K1[0..1], K2[0..1], V[0..1]
+  static_assert(sizeof(FullLds) == 6 * SLOT, "ring slots are contiguous");
+  const unsigned lds_w = lds_addr(&sm.K1[0][0]) + 8 * w * HD * 2;  // this wave's rows in slot 0
+  auto dma = [&](const u32x4_t& r, int doff, int u, int slot) {
+    load16_to_lds(rsrc_advance(r, (unsigned)(t_lo + u) * SLOT), doff, lds_w + slot * SLOT);
   };
+  constexpr int K1S = 0, K2S = 2, VR = 4;  // first slot of each ring
   // the first two key tiles, requested before anything else so that their latency overlaps the
   // query loads and the query preparation
-  dma(k1rs, doff_k, 0, sm.K1[0]);
-  dma(k2rs, doff_k, 0, sm.K2[0]);
-  dma(k1rs, doff_k, 1, sm.K1[1]);  // past the last tile: zeros, never read
-  dma(k2rs, doff_k, 1, sm.K2[1]);
+  dma(k1rs, doff_k, 0, K1S);
+  dma(k2rs, doff_k, 0, K2S);
+  dma(k1rs, doff_k, 1, K1S + 1);  // past the last tile: zeros, never read
+  dma(k2rs, doff_k, 1, K2S + 1);
   f16x8 Qf[NQB][2];
   {
     // this branch's queries (q1 with set 0, or q2 with set 2), requested before the parameters are
@@ -701,10 +707,10 @@ void diff_flash_duo(DiffArgs a, int nqb) {
     // (K(t) for S(t), V(t - 2) for the P.V of step t - 1); they are waited for before this step's
     // barrier
     if (t + 2 < T) {
-      dma(k1rs, doff_k, t + 2, sm.K1[PAR]);
-      dma(k2rs, doff_k, t + 2, sm.K2[PAR]);
+      dma(k1rs, doff_k, t + 2, K1S + PAR);
+      dma(k2rs, doff_k, t + 2, K2S + PAR);
     }
-    dma(vrs, doff_v, t, sm.V[PAR]);
+    dma(vrs, doff_v, t, VR + PAR);
     f16x8 kf[2][2], vf[4];
     if (NEXT) {
 #pragma unroll

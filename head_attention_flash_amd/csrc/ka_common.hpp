@@ -137,6 +137,20 @@ __device__ __forceinline__ u32x4_t raw_rsrc(const void* base, int bytes) {
   r[3] = RSRC_FLAGS;
   return r;
 }
+// The same buffer moved on by off bytes (off >= 0, wave-uniform): the base advanced and the size
+// shrunk, to zero past the end, so offsets past the end still read zeros.  Scalar arithmetic, so
+// that a loop can step a tile offset without a per-lane add.
+__device__ __forceinline__ u32x4_t rsrc_advance(u32x4_t r, unsigned off) {
+  const unsigned long long b = ((unsigned long long)r[1] << 32 | r[0]) + off;
+  // every word through readfirstlane: the descriptor operand must stay in scalar registers
+  u32x4_t n;
+  n[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
+  n[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  const int rem = (int)r[2] - (int)off;  // buffers stay below 2 GiB
+  n[2] = __builtin_amdgcn_readfirstlane(rem > 0 ? rem : 0);
+  n[3] = r[3];
+  return n;
+}
 // 16 bytes per lane from the buffer (offsets past its size read as zero) straight into LDS, lane l's
 // bytes at lds_base + 16 l.  M0 carries the wave's LDS base and is restored afterwards.  Inline
 // assembly, so that the compiler does not make every later LDS read wait for the load: the caller
