@@ -800,6 +800,9 @@ __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __re
   };
   bf16x8 Qc[2], Qn[2];
   qload(0, Qc);
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   {
     // every key and value of this (b, h); rows past Sk read as zero through the buffer
     // resources (their scores are masked)
@@ -842,28 +845,26 @@ __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __re
         S[kb_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, Qc[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         S[kb_] = mfma_bf16(a1, Qc[1], S[kb_]);
       }
-      if (Sk < NK) {  // padded keys are set to -inf before the maximum is taken
+      // padded keys are set to -inf before the maximum is taken; only a 16-key block that reaches
+      // past Sk holds any (a wave-uniform test per block)
 #pragma unroll
-        for (int kb_ = 0; kb_ < NKB; ++kb_)
+      for (int kb_ = 0; kb_ < NKB; ++kb_)
+        if (16 * kb_ + 16 > Sk) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[kb_][e] = 16 * kb_ + 4 * grp + e < Sk ? S[kb_][e] : -INFINITY;
-      }
+        }
       float mx = S[0][0];
 #pragma unroll
       for (int kb_ = 0; kb_ < NKB; ++kb_)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, S[kb_][e]);
       const float mc = group4_max(mx) * c;
-      float ls = 0.0f;
 #pragma unroll
       for (int kb_ = 0; kb_ < NKB; ++kb_)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(S[kb_][e], c, -mc));
-          S[kb_][e] = p;
-          ls += p;
-        }
-      l = group4_sum(ls);
+        for (int e = 0; e < 4; ++e) S[kb_][e] = fast_exp2(__builtin_fmaf(S[kb_][e], c, -mc));
+      // the row sum from an all-ones MFMA over the same bf16 weights as P.V
+      f32x4 L = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKB / 2; ++ks) {
         const bf16x8 P = pack_bf16(S[2 * ks], S[2 * ks + 1]);
@@ -875,7 +876,9 @@ __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __re
               cat_bf16(lds_read_tr16(&Vs[vrow * VP + vcol]), lds_read_tr16(&Vs[(vrow + 16) * VP + vcol]));
           O[db] = mfma_bf16(a, P, O[db]);
         }
+        L = mfma_bf16(ones, P, L);
       }
+      l = L[0];
     } else {
       float m = -INFINITY, lp = 0.0f;  // running maximum; this lane's share of the running sum
       const int nch = (Sk + 63) >> 6;
