@@ -106,37 +106,40 @@ __device__ __forceinline__ size_t slice_at(const DiffArgs& a, int t, size_t b, s
 // bytes a buffer resource over one slice spans: S rows at stride st[t], the last one 128 bytes
 __device__ __forceinline__ int slice_bytes(const DiffArgs& a, int t) { return ((a.S - 1) * a.st[t] + HD) * 2; }
 
-// Lanes holding one head row: four consecutive lanes (RED_QUAD) or {l, l^16, l^32,
-// l^48} (RED_GROUP4).
-constexpr int RED_QUAD = 0, RED_GROUP4 = 1;
+// Lanes holding one head row: four consecutive lanes (RED_QUAD), eight (RED_OCT) or {l, l^16,
+// l^32, l^48} (RED_GROUP4).
+constexpr int RED_QUAD = 0, RED_GROUP4 = 1, RED_OCT = 2;
 template <int RED>
 __device__ __forceinline__ float row_sum(float x) {
   if constexpr (RED == RED_QUAD) return quad_sum(x);
-  else return group4_sum(x);
+  else if constexpr (RED == RED_OCT) {
+    const float y = quad_sum(x);  // then the other quad of the eight (lane ^ 4, swizzle bit mode)
+    return y + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(y), 0x101F));
+  } else return group4_sum(x);
 }
 
-// Normalise (DyT, or RMSNorm over the row's 64 dims held by four lanes), then rotate,
-// 8 rotary pairs (dims d0+e and d0+gap+e, pair index i0+e) of two tensors (parameter
-// sets ta and tb) at the same position p; the angles are shared.  ONE: tensor a only.
-template <int NORM, int RED, bool ONE = false>
+// Normalise (DyT, or RMSNorm over the row's 64 dims held by the lanes RED names), then rotate,
+// NP rotary pairs (dims d0+e and d0+gap+e, pair index i0+e) of two tensors (parameter sets ta
+// and tb) at the same position p; the angles are shared.  ONE: tensor a only.
+template <int NORM, int RED, bool ONE = false, int NP = 8>
 __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int d0, int gap, int i0,
                                             int p, int ta, int tb, const SharedParams& sp) {
   const float pf = (float)p;
-  // one uniform branch for all eight angles, so that the straight-line DyT and rotation
+  // one uniform branch for all the angles, so that the straight-line DyT and rotation
   // below form one block the scheduler can interleave
-  float csv[8], snv[8];
+  float csv[NP], snv[NP];
   if (sp.split) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rope_cs_split(pf, sp.rev_hi[i0 + e], sp.rev_lo[i0 + e], csv[e], snv[e]);
+    for (int e = 0; e < NP; ++e) rope_cs_split(pf, sp.rev_hi[i0 + e], sp.rev_lo[i0 + e], csv[e], snv[e]);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rope_cs_f64(p, sp.rev[i0 + e], csv[e], snv[e]);
+    for (int e = 0; e < NP; ++e) rope_cs_f64(p, sp.rev[i0 + e], csv[e], snv[e]);
   }
   float ra = 1.0f, rb = 1.0f;  // RMSNorm: 1 / sqrt(mean x^2 + eps) of each row
   if constexpr (NORM == NORM_RMS) {
     float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NP; ++e) {
       sa = __builtin_fmaf(alo[e], alo[e], __builtin_fmaf(ahi[e], ahi[e], sa));
       if (!ONE) sb = __builtin_fmaf(blo[e], blo[e], __builtin_fmaf(bhi[e], bhi[e], sb));
     }
@@ -145,7 +148,7 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
   }
   const float ka = sp.k2a[ta], kb = sp.k2a[tb];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < NP; ++e) {
     const int dl = d0 + e, dh = d0 + gap + e;
     const float cs = csv[e], sn = snv[e];
     auto norm = [&](float x, int t, int d, float k, float r) {
@@ -179,6 +182,14 @@ __device__ __forceinline__ f16x8 to_f16x8(const float* f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (_Float16)pin(f[e]);
   return r;
+}
+// the same rounding for four values, as their bits
+__device__ __forceinline__ uint2 to_f16x4_bits(const float* f) {
+  typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+  f16x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (_Float16)pin(f[e]);
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Load dims [d0, d0+8) and [d0+gap, d0+gap+8) of one bf16 row as fp32 (zeros if !ok).
@@ -468,15 +479,17 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   const size_t row0 = (size_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const bool live = row0 < nrows;
   const size_t row = live ? row0 : nrows - 1;  // lanes past the end load a valid row, store nothing
-  const int sub = threadIdx.x & 7, tk = sub >> 2, cc = sub & 3;  // tensor (0: k1, 1: k2), chunk
+  // lane sub of the octet: rotary pairs 4 sub .. 4 sub + 3 of both k1 and k2 (dims d0 .. d0 + 3 and
+  // the four they pair with), so the angles are computed once for the two tensors
+  const int sub = threadIdx.x & 7;
   const int j = (int)(row % (size_t)a.S);
   const size_t h = (row / a.S) % a.H, bb = row / a.S / a.H;
   const bool rot32 = a.rot32 != 0;
-  const int gap = pair_gap(rot32), d0 = lo_dim(cc, rot32);
-  const int t = tk ? TK2 : TK1;
+  const int gap = pair_gap(rot32), d0 = rot32 && sub >= 4 ? 4 * sub + 16 : 4 * sub;
   // the row's loads are issued before the parameters are staged, so the two latencies overlap
-  float lo[8], hi[8];
-  load_pairs((tk ? a.k2 : a.k1) + slice_at(a, t, bb, h) + (size_t)j * a.st[t], d0, gap, true, lo, hi);
+  const unsigned short* k1r = a.k1 + slice_at(a, TK1, bb, h) + (size_t)j * a.st[TK1];
+  const unsigned short* k2r = a.k2 + slice_at(a, TK2, bb, h) + (size_t)j * a.st[TK2];
+  const uint2 u1l = ld8(k1r + d0), u1h = ld8(k1r + d0 + gap), u2l = ld8(k2r + d0), u2h = ld8(k2r + d0 + gap);
   // V row: 8 values per thread
   const unsigned short* vr = a.v + slice_at(a, TV, bb, h) + (size_t)j * a.st[TV];
   const uint4 vx = ld16(vr + 8 * sub);
@@ -484,10 +497,19 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   load_params<NORM>(sp, a);
   __syncthreads();
   if (!live) return;  // whole octets: the lanes of a row leave together
-  prep_pairs2<NORM, RED_QUAD, true>(lo, hi, lo, hi, d0, gap, 8 * cc, j, tk ? 3 : 1, tk ? 3 : 1, sp);
-  _Float16* w = a.ws + (size_t)tk * nrows * HD + row * HD;
-  st16(w + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(lo)));
-  st16(w + 32 + 8 * cc, __builtin_bit_cast(uint4, to_f16x8(hi)));
+  float alo[4], ahi[4], blo[4], bhi[4];
+  unpack_bf16x4(u1l, alo);
+  unpack_bf16x4(u1h, ahi);
+  unpack_bf16x4(u2l, blo);
+  unpack_bf16x4(u2h, bhi);
+  prep_pairs2<NORM, RED_OCT, false, 4>(alo, ahi, blo, bhi, d0, gap, 4 * sub, j, 1, 3, sp);
+  // the planes hold pair i's rotated dims at i and 32 + i (the layout of the queries' fragments)
+  _Float16* w1 = a.ws + row * HD + 4 * sub;
+  _Float16* w2 = w1 + nrows * HD;
+  st8(w1, to_f16x4_bits(alo));
+  st8(w1 + 32, to_f16x4_bits(ahi));
+  st8(w2, to_f16x4_bits(blo));
+  st8(w2 + 32, to_f16x4_bits(bhi));
   // V as fp16 for pass 2's P.V (exact for 2^-14 <= |v| <= 65504: a bf16 value has 8 significant
   // bits, fp16 11), with the rows of flagged-out tokens zeroed
   const unsigned m = keep ? ~0u : 0u;

@@ -174,6 +174,7 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // Unpack 8 bf16 (one uint4) into fp32.
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
@@ -183,6 +184,14 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float* f) {
     f[2 * i] = __uint_as_float(w[i] << 16);
     f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
+}
+
+// Unpack 4 bf16 (one uint2) into fp32.
+__device__ __forceinline__ void unpack_bf16x4(const uint2& u, float* f) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
 // Four fp32 -> four bf16 packed into 8 bytes.
