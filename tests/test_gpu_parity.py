@@ -139,6 +139,27 @@ def test_dense_bf16_peaked_large(B, H, Sq, Sk, qscale):
     _parity(got, oracle.attn(q, k, v, wl.scale), bits, f"bf16 peaked x{qscale} {B}x{H}x{Sq}x{Sk}")
 
 
+@pytest.mark.parametrize("B,H,Sq,Sk,Dh,step", [(1, 2, 256, 1024, 64, 9.0), (1, 2, 256, 1024, 64, -9.0),
+                                              (2, 10, 4096, 512, 64, 9.0), (1, 1, 200, 512, 512, 9.0)])
+def test_dense_score_ramp(B, H, Sq, Sk, Dh, step):
+    """Scores that rise by `step` (in the exp2 domain) from each 32-key tile to the next: every tile's
+    maximum passes the running one by more than the lazy threshold (8), so the kernels raise their
+    reference and rescale O and l on every tile; a falling ramp raises only on the first.  Keys are
+    a per-tile multiple of q plus noise; every output element against the oracle."""
+    scale = Dh ** -0.5
+    c = scale * np.log2(np.e)
+    r = np.random.default_rng(4100 + Sk + Dh + int(step))
+    tile = np.arange(Sk) // 32
+    a = step * (tile - (tile.max() if step < 0 else 0)) / (c * Dh)  # c q.k = step * tile (+ const)
+    qf = np.ones((B, H, Sq, Dh), np.float32) + 0.05 * r.standard_normal((B, H, Sq, Dh)).astype(np.float32)
+    kf = a[None, None, :, None] + 0.05 * r.standard_normal((B, H, Sk, Dh))
+    q = synth.f32_to_bf16_bits(qf)
+    k = synth.f32_to_bf16_bits(kf.astype(np.float32))
+    v = synth.f32_to_bf16_bits(r.standard_normal((B, H, Sk, Dh)).astype(np.float32))
+    got = _run_dense(ka.ka_attn_fwd, q, k, v, scale)
+    assert_close(got, oracle.attn(q, k, v, scale), BF16_TOL, f"ramp {step:+} {B}x{H}x{Sq}x{Sk} d{Dh}")
+
+
 @pytest.mark.parametrize("Sq", [370, 2000])
 def test_dense_layouts_agree(Sq):
     """Tile independence: one (b, h) slice copied into batches whose size selects each dense layout
