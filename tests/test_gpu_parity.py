@@ -444,6 +444,38 @@ def test_diff_model_forms(norm, rot, padded, window):
     assert_close(got, want, BF16_TOL, f"model form norm={norm} rot={rot} padded={padded} w={window}")
 
 
+@pytest.mark.parametrize("window", [-1, 200])
+@pytest.mark.parametrize("step", [15.0, -15.0])
+def test_diff_score_ramp(window, step):
+    """Branch-1 scores that rise by `step` (in the exp2 domain) from each 32-key tile to the next,
+    past the full path's lazy threshold (14), so its weights are rescaled on every tile (a falling
+    ramp: only on the first).  Built without the rotation's mixing: rotary on dims 0-31 only, the
+    signal in the unrotated dims 32-63; DyT with beta = 0 and gamma = 4 saturates the queries to +4
+    and maps each key tile to one level of 4 tanh(k).  Every output element against the oracle."""
+    S, H, B = 400, 2, 1
+    c = 0.125 * np.log2(np.e)
+    r = np.random.default_rng(5100 + int(step) + max(window, 0))
+    tile = np.arange(S) // 32
+    ntile = tile.max()
+    lev = (-0.975 + 1.95 * tile / ntile) if step > 0 else (0.975 - 1.95 * tile / ntile)
+    assert abs(c * 32 * 16 * 1.95 / ntile - abs(step)) < 0.1  # c q^.k^ moves by `step` per tile
+    q1 = np.zeros((B, H, S, D), np.float32)
+    q1[..., 32:] = 10.0
+    k1 = np.zeros((B, H, S, D), np.float32)
+    k1[..., 32:] = np.arctanh(lev)[None, None, :, None] + 0.01 * r.standard_normal((B, H, S, 32))
+    q2, k2, v = (r.standard_normal((B, H, S, D)).astype(np.float32) for _ in range(3))
+    inputs = tuple(synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q1, k1, q2, k2, v))
+    alpha = np.array([1.0, 1.0, 0.5, 0.5], np.float32)
+    gamma = np.ones((4, D), np.float32)
+    gamma[:2] = 4.0
+    beta = np.zeros((4, D), np.float32)
+    lam = np.full(H, 0.8, np.float32)
+    params = (alpha, gamma, beta, lam)
+    got = _run_diff_ex(inputs, params, window, "dyt", 32, None)
+    want = _oracle_diff_ex(inputs, params, window, "dyt", 32, None)
+    assert_close(got, want, BF16_TOL, f"diff ramp {step:+} w={window}")
+
+
 @pytest.mark.parametrize("norm", ["dyt", "rms"])
 def test_diff_model_band_strips(norm):
     """RMSNorm's row reductions in the key ring fill and the per-block staging, many strips."""
