@@ -199,18 +199,24 @@ void attn512_pair(const unsigned short* __restrict__ q, const unsigned short* __
   for (int e = 0; e < 4; ++e) ones[e] = (short)0x3F80;  // bf16 1.0
 
   // tile tt (16 keys) of this half into buffer buf: the half's four waves move rows wq, wq + 4, ..
-  // of K and V, one 1 KB row per instruction; rows past Sk repeat row Sk - 1 (masked, weight 0)
-  const unsigned short* kb = k + bh * (size_t)Sk * D5;
-  const unsigned short* vb = v + bh * (size_t)Sk * D5;
+  // of K and V, one 1 KB row per instruction (lane l's 16 bytes at the row base + 16 l); rows
+  // past Sk read as zero through the descriptors (their scores are masked).  Inline assembly with
+  // the tile offset in the descriptor and the slot in M0: the compiler does not make the V reads
+  // of the current tile wait for the next tile's loads.
   const int T16 = (Sk + BP5 - 1) / BP5;          // 16-key tiles
   const int NS = (T16 + 1) / 2;                  // steps: tiles 2s (half 0) and 2s + 1 (half 1)
+  const u32x4_t krs = raw_rsrc(k + bh * (size_t)Sk * D5, Sk * D5 * 2);
+  const u32x4_t vrs = raw_rsrc(v + bh * (size_t)Sk * D5, Sk * D5 * 2);
+  const unsigned ldsK = lds_addr(&sm.K[half][0][0]), ldsV = lds_addr(&sm.V[half][0][0]);
+  constexpr unsigned KT = BP5 * KP5 * 2, VT = BP5 * VP5 * 2;  // bytes of a tile buffer
   auto tile_load = [&](int tt, int buf) {
+    const u32x4_t kr = rsrc_advance(krs, (unsigned)tt * (BP5 * D5 * 2));
+    const u32x4_t vr = rsrc_advance(vrs, (unsigned)tt * (BP5 * D5 * 2));
 #pragma unroll
     for (int i = 0; i < BP5 / 4; ++i) {
       const int row = wq + 4 * i;
-      const size_t j = (size_t)min(tt * BP5 + row, Sk - 1);
-      __builtin_amdgcn_global_load_lds(kb + j * D5 + 8 * lane, (lds_void*)&sm.K[half][buf][row * KP5], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + j * D5 + 8 * lane, (lds_void*)&sm.V[half][buf][row * VP5], 16, 0, 0);
+      load16_to_lds(kr, row * (D5 * 2) + 16 * lane, ldsK + buf * KT + row * (KP5 * 2));
+      load16_to_lds(vr, row * (D5 * 2) + 16 * lane, ldsV + buf * VT + row * (VP5 * 2));
     }
   };
   if (half < T16) tile_load(half, 0);
