@@ -401,7 +401,7 @@ def main():
         f = acc.attn_flops(wl.B, wl.H, wl.Sq, wl.Sk, D=wl.D)
         sec = time_launches(lambda i: ka.ka_attn_fwd(q5, k5, v5, o=o5, scale=wl.scale), 1, max(5, args.steps // 5),
                             args.warmup, torch)
-        forms["vae_mid"] = {"workload": wl.key, "kernel": "attn512_bf16", "us": round(sec * 1e6, 3),
+        forms["vae_mid"] = {"workload": wl.key, "kernel": "attn512_pair", "us": round(sec * 1e6, 3),
                             "TFLOP/s": round(f / sec / 1e12, 3), "mfma_frac": round(f / sec / acc.MFMA_BF16_PEAK, 4),
                             "bound": "mfma", "flops": f}
         log(f"bench: vae_mid {forms['vae_mid']}")

@@ -316,7 +316,7 @@ const char* ka_attn_kernel_name(ka_dtype dtype, int B, int H, int Sq, int Sk, in
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || !grid_ok(B, H, Sq)) return nullptr;
   if (dtype == KA_F32 && D == 64) return "attn_f32";
   if (dtype != KA_BF16) return nullptr;
-  if (D == 512) return "attn512_bf16";
+  if (D == 512) return "attn512_pair";
   if (D != 64) return nullptr;
   return ka::attn_bf16_kernel_name(B, H, Sq);
 }

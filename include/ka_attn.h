@@ -203,7 +203,7 @@ size_t ka_diffattn_workspace_bytes(int B, int H, int S, int D, int window);
 
 /* Name of the kernel (and query layout) ka_attn_fwd launches for this shape on the
  * current device, e.g. "attn_bf16_quad 3+2", "attn_bf16_duo 3+3", "attn_bf16_pipe",
- * "attn_f32", "attn512_bf16"; NULL for a shape or dtype ka_attn_fwd rejects.  A static
+ * "attn_f32", "attn512_pair"; NULL for a shape or dtype ka_attn_fwd rejects.  A static
  * string.  For tuning and for checks that every layout computes the same result. */
 const char* ka_attn_kernel_name(ka_dtype dtype, int B, int H, int Sq, int Sk, int D);
 

@@ -229,7 +229,7 @@ def test_kernel_name_introspection(lib):
     assert name(ka.KA_BF16, 1, 1, 100, 100, 64) == b"attn_bf16_pipe"
     assert name(ka.KA_BF16, 1, 256, 370, 333, 64) == b"attn_bf16_duo 3+3"
     assert name(ka.KA_F32, 1, 2, 256, 256, 64) == b"attn_f32"
-    assert name(ka.KA_BF16, 1, 1, 16384, 16384, 512) == b"attn512_bf16"
+    assert name(ka.KA_BF16, 1, 1, 16384, 16384, 512) == b"attn512_pair"
     assert name(ka.KA_F32, 1, 1, 16, 16, 512) is None
     assert name(ka.KA_BF16, 0, 1, 16, 16, 64) is None
     assert name(ka.KA_BF16, 1, 1 << 23, 1, 1, 64) is None
