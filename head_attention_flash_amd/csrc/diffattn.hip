@@ -535,8 +535,9 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
 // by F_LAZY: a packed 16-bit maximum over the fp16 weights and a wave-wide vote replace the
 // per-tile maximum, and only a voting wave takes maxima and raises R (per query, from its own
 // scores).  DyT scores spread widely (a standard deviation near 7 in the exp2 domain): with a
-// threshold of 8 a fifth of the wave-steps raise, with 14 about one in thirty; fp16 holds
-// weights up to 2^15.
+// threshold of 8 a fifth of the wave-steps raise, with 14 about one in thirty; 15 is the largest
+// whose weights fp16 still holds (a larger weight converts, toward zero, to 65504, which still
+// votes).
 // P and V meet as fp16 (the prepared V plane): half the rounding of bf16 weights.  The row sum
 // comes from an all-ones MFMA over the same fp16 weights, so O / l is a convex combination.
 // At the end branch-2 waves leave lambda O2 / l2 in LDS and branch-1 waves subtract it.
@@ -561,8 +562,8 @@ constexpr int F_VLEAD = F_VLEAD_SET;  // vector work runs this many slots ahead 
 #define FULL_WPE 3
 #endif
 constexpr float R_NONE = -1e30f;  // reference of a query that has seen no key (finite: -inf - -inf = NaN)
-constexpr float F_LAZY = 14.0f;   // raise threshold (exp2 domain): weights stay below 2^14
-constexpr unsigned short F_VOTE = 0x7400;  // fp16 bit pattern of 2^14
+constexpr float F_LAZY = 15.0f;   // raise threshold (exp2 domain): weights stay below 2^15
+constexpr unsigned short F_VOTE = 0x7800;  // fp16 bit pattern of 2^15
 
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
 // Some fp16 half of the four words is >= 2^F_LAZY (non-negative fp16 values order like their
