@@ -21,9 +21,9 @@ constexpr int VP5 = D5 + 16;      // LDS pitch of V (elements), as VP for the tr
 
 // Two waves per SIMD by splitting the keys: a block of eight waves serves 64 queries, waves w and
 // w + 4 the same 16 (w % 4), wave w taking the even and wave w + 4 the odd 16-key tiles of
-// every 32 keys.  Each half has its own double-buffered K and V tiles in LDS (134 KB in all, one
-// block per CU as before), so the second wave of a SIMD covers the first one's LDS and MFMA
-// latencies.  Per 16-key tile a wave issues 16 MFMAs 16x16x32 for S^T and 32 MFMAs 16x16x16
+// every 32 keys.  Each half has its own double-buffered K and V tiles in LDS (134 KB in all: one
+// block per CU, 256 blocks for the 16384-token head), so the second wave of a SIMD covers the
+// first one's LDS and MFMA latencies.  Per 16-key tile a wave issues 16 MFMAs 16x16x32 for S^T and 32 MFMAs 16x16x16
 // for O^T (the weights of 16 keys are one B operand).  At the end the odd-tile waves leave
 // (m, l, O) in LDS and the even-tile waves merge them with the online-softmax rescale.
 constexpr int BP5 = 16;  // keys per tile and half
