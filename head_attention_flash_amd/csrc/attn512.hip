@@ -147,17 +147,17 @@ void attn512_pair(const unsigned short* __restrict__ q, const unsigned short* __
 
   // merge: the odd-tile waves leave m, l and O in LDS (over the tile buffers, no longer read after
   // the last barrier); the even-tile waves rescale both to the larger maximum and add
-  // [4 waves][64 lanes][128] O (16-byte aligned rows), then [4][64][2] m and l
-  float* X = reinterpret_cast<float*>(&sm);
+  // O as [4 waves][32 dim blocks][64 lanes] f32x4 (a wave's accesses to one block are one
+  // contiguous 1 KB, free of bank conflicts), then m and l as [4][64][2]
+  f32x4* XO = reinterpret_cast<f32x4*>(&sm);
   static_assert(sizeof(LdsPair512) >= 4 * 64 * (D5 / 4 + 2) * 4, "the merge area fits the tiles");
-  const int xi = wq * 64 + lane;
-  float* xo = X + (size_t)xi * (D5 / 4);
-  float* xm = X + 4 * 64 * (D5 / 4) + 2 * xi;
+  auto xo = [&](int db) -> f32x4& { return XO[(wq * (D5 / 16) + db) * 64 + lane]; };
+  float* xm = reinterpret_cast<float*>(XO + 4 * (D5 / 16) * 64) + 2 * (wq * 64 + lane);
   if (half) {
     xm[0] = m;
     xm[1] = L[0];
 #pragma unroll
-    for (int db = 0; db < D5 / 16; ++db) *reinterpret_cast<f32x4*>(&xo[4 * db]) = O[db];
+    for (int db = 0; db < D5 / 16; ++db) xo(db) = O[db];
   }
   __syncthreads();
   if (half) return;
@@ -169,7 +169,7 @@ void attn512_pair(const unsigned short* __restrict__ q, const unsigned short* __
   if (row < Sq) {
 #pragma unroll
     for (int db = 0; db < D5 / 16; ++db) {
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(&xo[4 * db]);
+      const f32x4 o1 = xo(db);
       f32x4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = (O[db][e] * a0 + o1[e] * a1) * inv;
