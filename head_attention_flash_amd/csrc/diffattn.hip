@@ -118,22 +118,89 @@ __device__ __forceinline__ float row_sum(float x) {
   } else return group4_sum(x);
 }
 
+// The parameters as the preparation reads them: staged in LDS for the whole workgroup ...
+struct LdsParamView {
+  const SharedParams& sp;
+  __device__ bool split() const { return sp.split; }
+  __device__ float rev_hi(int i, int) const { return sp.rev_hi[i]; }
+  __device__ float rev_lo(int i, int) const { return sp.rev_lo[i]; }
+  __device__ double rev(int i, int) const { return sp.rev[i]; }
+  __device__ float eps() const { return sp.eps; }
+  __device__ float k2a(int t) const { return sp.k2a[t]; }
+  __device__ float gpb(int t, int d, int, int) const { return sp.gpb[t][d]; }
+  __device__ float m2g(int t, int d, int, int) const { return sp.m2g[t][d]; }
+};
+// ... or loaded by each thread for its own NP rotary pairs (dims d0 + e and d0 + gap + e) of NSET
+// parameter sets straight from global memory (the key-prep pass: k1 and k2; the flash pass: its
+// branch's queries): no LDS staging and no barrier before the preparation.
+template <int NORM, int NP, int NSET>
+struct RegParams {
+  float g[NSET][2][NP], b[NSET][2][NP];  // gamma (or the RMS weight) and beta of dims d0 + e, d0 + gap + e
+  float rhi[NP], rlo[NP];
+  double rv[NP];
+  float ka[NSET];
+  int t0;  // set of slot 0; slot 1 (when NSET = 2) holds set t0 + 2
+  float ep;
+  int sp_;
+  __device__ RegParams(const DiffArgs& a, int d0, int gap, int i0, int first_set) : t0(first_set) {
+    static_assert(NP % 4 == 0, "parameters are read as float4");
+#pragma unroll
+    for (int s2 = 0; s2 < NSET; ++s2) {
+      const int t = first_set + 2 * s2;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e4 = 0; e4 < NP; e4 += 4) {
+          const int d = d0 + hh * gap + e4;
+          const float4 gv = *reinterpret_cast<const float4*>((NORM == NORM_RMS ? a.rms_w : a.gamma) + t * HD + d);
+          g[s2][hh][e4] = gv.x; g[s2][hh][e4 + 1] = gv.y; g[s2][hh][e4 + 2] = gv.z; g[s2][hh][e4 + 3] = gv.w;
+          if constexpr (NORM == NORM_DYT) {
+            const float4 bv = *reinterpret_cast<const float4*>(a.beta + t * HD + d);
+            b[s2][hh][e4] = bv.x; b[s2][hh][e4 + 1] = bv.y; b[s2][hh][e4 + 2] = bv.z; b[s2][hh][e4 + 3] = bv.w;
+          }
+        }
+      ka[s2] = NORM == NORM_DYT ? 2.0f * LOG2E * a.alpha[t] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      rhi[e] = a.rev_hi[i0 + e];
+      rlo[e] = a.rev_lo[i0 + e];
+      rv[e] = a.rev[i0 + e];
+    }
+    ep = a.rms_eps;
+    sp_ = a.split_angles;
+  }
+  __device__ int slot(int t) const { return NSET == 1 ? 0 : (t != t0); }
+  __device__ bool split() const { return sp_; }
+  __device__ float rev_hi(int, int e) const { return rhi[e]; }
+  __device__ float rev_lo(int, int e) const { return rlo[e]; }
+  __device__ double rev(int, int e) const { return rv[e]; }
+  __device__ float eps() const { return ep; }
+  __device__ float k2a(int t) const { return ka[slot(t)]; }
+  // the values load_params stages: gamma + beta and -2 gamma (DyT), the weight (RMSNorm)
+  __device__ float gpb(int t, int, int e, int hh) const {
+    return NORM == NORM_RMS ? g[slot(t)][hh][e] : g[slot(t)][hh][e] + b[slot(t)][hh][e];
+  }
+  __device__ float m2g(int t, int, int e, int hh) const { return -2.0f * g[slot(t)][hh][e]; }
+};
+
 // Normalise (DyT, or RMSNorm over the row's 64 dims held by the lanes RED names), then rotate,
 // NP rotary pairs (dims d0+e and d0+gap+e, pair index i0+e) of two tensors (parameter sets ta
-// and tb) at the same position p; the angles are shared.  ONE: tensor a only.
-template <int NORM, int RED, bool ONE = false, int NP = 8>
+// and tb) at the same position p; the angles are shared.  ONE: tensor a only.  PV: where the
+// parameters come from (LdsParamView or RegParams).
+template <int NORM, int RED, bool ONE = false, int NP = 8, class PV>
 __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, float* bhi, int d0, int gap, int i0,
-                                            int p, int ta, int tb, const SharedParams& sp) {
+                                            int p, int ta, int tb, const PV& sp) {
   const float pf = (float)p;
   // one uniform branch for all the angles, so that the straight-line DyT and rotation
   // below form one block the scheduler can interleave
   float csv[NP], snv[NP];
-  if (sp.split) {
+  if (sp.split()) {
 #pragma unroll
-    for (int e = 0; e < NP; ++e) rope_cs_split(pf, sp.rev_hi[i0 + e], sp.rev_lo[i0 + e], csv[e], snv[e]);
+    for (int e = 0; e < NP; ++e) rope_cs_split(pf, sp.rev_hi(i0 + e, e), sp.rev_lo(i0 + e, e), csv[e], snv[e]);
   } else {
 #pragma unroll
-    for (int e = 0; e < NP; ++e) rope_cs_f64(p, sp.rev[i0 + e], csv[e], snv[e]);
+    for (int e = 0; e < NP; ++e) rope_cs_f64(p, sp.rev(i0 + e, e), csv[e], snv[e]);
   }
   float ra = 1.0f, rb = 1.0f;  // RMSNorm: 1 / sqrt(mean x^2 + eps) of each row
   if constexpr (NORM == NORM_RMS) {
@@ -143,24 +210,24 @@ __device__ __forceinline__ void prep_pairs2(float* alo, float* ahi, float* blo, 
       sa = __builtin_fmaf(alo[e], alo[e], __builtin_fmaf(ahi[e], ahi[e], sa));
       if (!ONE) sb = __builtin_fmaf(blo[e], blo[e], __builtin_fmaf(bhi[e], bhi[e], sb));
     }
-    ra = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sa), 1.0f / HD, sp.eps));
-    if (!ONE) rb = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sb), 1.0f / HD, sp.eps));
+    ra = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sa), 1.0f / HD, sp.eps()));
+    if (!ONE) rb = __builtin_amdgcn_rsqf(__builtin_fmaf(row_sum<RED>(sb), 1.0f / HD, sp.eps()));
   }
-  const float ka = sp.k2a[ta], kb = sp.k2a[tb];
+  const float ka = sp.k2a(ta), kb = sp.k2a(tb);
 #pragma unroll
   for (int e = 0; e < NP; ++e) {
     const int dl = d0 + e, dh = d0 + gap + e;
     const float cs = csv[e], sn = snv[e];
-    auto norm = [&](float x, int t, int d, float k, float r) {
-      if constexpr (NORM == NORM_RMS) return sp.gpb[t][d] * (x * r);
-      else return dyt(x, k, sp.gpb[t][d], sp.m2g[t][d]);
+    auto norm = [&](float x, int t, int d, int hh, float k, float r) {
+      if constexpr (NORM == NORM_RMS) return sp.gpb(t, d, e, hh) * (x * r);
+      else return dyt(x, k, sp.gpb(t, d, e, hh), sp.m2g(t, d, e, hh));
     };
-    const float a0 = norm(alo[e], ta, dl, ka, ra), a1 = norm(ahi[e], ta, dh, ka, ra);
+    const float a0 = norm(alo[e], ta, dl, 0, ka, ra), a1 = norm(ahi[e], ta, dh, 1, ka, ra);
     // explicit fused forms: every tensor rounds identically, whatever the compiler would contract
     alo[e] = __builtin_fmaf(a0, cs, -(a1 * sn));
     ahi[e] = __builtin_fmaf(a1, cs, a0 * sn);
     if (!ONE) {
-      const float b0 = norm(blo[e], tb, dl, kb, rb), b1 = norm(bhi[e], tb, dh, kb, rb);
+      const float b0 = norm(blo[e], tb, dl, 0, kb, rb), b1 = norm(bhi[e], tb, dh, 1, kb, rb);
       blo[e] = __builtin_fmaf(b0, cs, -(b1 * sn));
       bhi[e] = __builtin_fmaf(b1, cs, b0 * sn);
     }
@@ -270,7 +337,7 @@ __device__ __forceinline__ void stage_commit(const RowStage& st, unsigned short*
   unpack_bf16x8(st.k2lo, k2lo);
   unpack_bf16x8(st.k2hi, k2hi);
   // rows no query of the strip sees are prepared too (finite, and masked in every tile)
-  prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, sp);
+  prep_pairs2<NORM, RED_QUAD>(k1lo, k1hi, k2lo, k2hi, d0, gap, 8 * cc, j, 1, 3, LdsParamView{sp});
   st16(&K1s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1lo)));
   st16(&K1s[slot * KPD + 32 + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k1hi)));
   st16(&K2s[slot * KPD + 8 * cc], __builtin_bit_cast(uint4, to_f16x8(k2lo)));
@@ -432,7 +499,7 @@ void diff_band(DiffArgs a, int nblk, int nstrip) {
     unpack_bf16x8(qs[1], q1hi);
     unpack_bf16x8(qs[2], q2lo);
     unpack_bf16x8(qs[3], q2hi);
-    prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, sp);
+    prep_pairs2<NORM, RED_GROUP4>(q1lo, q1hi, q2lo, q2hi, qd0, gap, 8 * grp, p, 0, 2, LdsParamView{sp});
     const f16x8 Q1[2] = {to_f16x8(q1lo), to_f16x8(q1hi)};
     const f16x8 Q2[2] = {to_f16x8(q2lo), to_f16x8(q2hi)};
     // fetch what the next block adds while this one computes
@@ -468,13 +535,14 @@ void diff_band(DiffArgs a, int nblk, int nstrip) {
 }
 
 // ---------------------------------------------------------------- full path, pass 1: key prep
-// Eight threads per key row: lanes 0-3 of the octet prepare k1 (8 rotary pairs each), lanes
-// 4-7 k2, and each converts 8 values of V to fp16.  (Four threads per row holding both
-// tensors left about 1.4 waves per SIMD for the 1422-token shape: too few to cover the load
-// and transcendental latencies of this short pass.)
+// Eight threads per key row: lane sub of the octet prepares rotary pairs 4 sub .. 4 sub + 3 of
+// both k1 and k2 (their angles computed once for the two tensors) and converts 8 values of V to
+// fp16.  Each thread reads its own parameters from global memory, so nothing waits for a
+// workgroup barrier.  (Four threads per row holding both tensors left about 1.4 waves per SIMD
+// for the 1422-token shape: too few to cover the load and transcendental latencies of this
+// short pass.)
 template <int NORM>
 __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
-  __shared__ SharedParams sp;
   const size_t nrows = (size_t)a.B * a.H * a.S;
   const size_t row0 = (size_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const bool live = row0 < nrows;
@@ -486,7 +554,7 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   const size_t h = (row / a.S) % a.H, bb = row / a.S / a.H;
   const bool rot32 = a.rot32 != 0;
   const int gap = pair_gap(rot32), d0 = rot32 && sub >= 4 ? 4 * sub + 16 : 4 * sub;
-  // the row's loads are issued before the parameters are staged, so the two latencies overlap
+  // the row's loads are issued before the parameter loads, so the two latencies overlap
   const unsigned short* k1r = a.k1 + slice_at(a, TK1, bb, h) + (size_t)j * a.st[TK1];
   const unsigned short* k2r = a.k2 + slice_at(a, TK2, bb, h) + (size_t)j * a.st[TK2];
   const uint2 u1l = ld8(k1r + d0), u1h = ld8(k1r + d0 + gap), u2l = ld8(k2r + d0), u2h = ld8(k2r + d0 + gap);
@@ -494,15 +562,14 @@ __global__ __launch_bounds__(256) void diff_kprep(DiffArgs a) {
   const unsigned short* vr = a.v + slice_at(a, TV, bb, h) + (size_t)j * a.st[TV];
   const uint4 vx = ld16(vr + 8 * sub);
   const bool keep = !a.v_keep || a.v_keep[bb * a.S + j] != 0;
-  load_params<NORM>(sp, a);
-  __syncthreads();
+  const RegParams<NORM, 4, 2> prm(a, d0, gap, 4 * sub, 1);  // sets 1 (k1) and 3 (k2)
   if (!live) return;  // whole octets: the lanes of a row leave together
   float alo[4], ahi[4], blo[4], bhi[4];
   unpack_bf16x4(u1l, alo);
   unpack_bf16x4(u1h, ahi);
   unpack_bf16x4(u2l, blo);
   unpack_bf16x4(u2h, bhi);
-  prep_pairs2<NORM, RED_OCT, false, 4>(alo, ahi, blo, bhi, d0, gap, 4 * sub, j, 1, 3, sp);
+  prep_pairs2<NORM, RED_OCT, false, 4>(alo, ahi, blo, bhi, d0, gap, 4 * sub, j, 1, 3, prm);
   // the planes hold pair i's rotated dims at i and 32 + i (the layout of the queries' fragments)
   _Float16* w1 = a.ws + row * HD + 4 * sub;
   _Float16* w2 = w1 + nrows * HD;
@@ -598,8 +665,7 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   static_assert(FBN * 8 == 256, "one 16-byte chunk of each tensor per thread and tile");
   static_assert(2 * 2 * FBN * HD * 2 >= 2 * NQB * 4 * 64 * 16, "the branch-2 hand-over must fit the K rings");
   __shared__ __align__(16) FullLds sm;
-  __shared__ SharedParams sp;
-
+  
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int br = w >> 1;  // 0: branch 1, 1: branch 2 (wave-uniform)
@@ -655,8 +721,8 @@ void diff_flash_duo(DiffArgs a, int nqb) {
   dma(k2rs, doff_k, 1, K2S + 1);
   f16x8 Qf[NQB][2];
   {
-    // this branch's queries (q1 with set 0, or q2 with set 2), requested before the parameters are
-    // staged so that the two latencies overlap
+    // this branch's queries (q1 with set 0, or q2 with set 2), then the lane's own parameters, both
+    // straight from global memory (their latencies overlap, and no barrier precedes the preparation)
     const int tq = br ? TQ2 : TQ1, set = br ? 2 : 0;
     const unsigned short* qt = br ? a.q2 : a.q1;
     float lo[NQB][8], hi[NQB][8];
@@ -666,12 +732,11 @@ void diff_flash_duo(DiffArgs a, int nqb) {
       const size_t pc = p < S ? p : 0;
       load_pairs(qt + slice_at(a, tq, bb, h) + pc * a.st[tq], qd0, gap, p < S, lo[i], hi[i]);
     }
-    load_params<NORM>(sp, a);
-    __syncthreads();
+    const RegParams<NORM, 8, 1> prm(a, qd0, gap, 8 * grp, set);
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
       prep_pairs2<NORM, RED_GROUP4, true>(lo[i], hi[i], lo[i], hi[i], qd0, gap, 8 * grp, q0 + 16 * i + col, set, set,
-                                          sp);
+                                          prm);
       Qf[i][0] = to_f16x8(lo[i]);
       Qf[i][1] = to_f16x8(hi[i]);
     }
