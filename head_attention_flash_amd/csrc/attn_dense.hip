@@ -376,12 +376,11 @@ void attn_bf16_pipe(const unsigned short* __restrict__ q,
   for (int i = 0; i < NQB; ++i) {
     const float inv = 1.0f / R.L[i][0];
     const int row = q0 + 16 * i + col;
-    if (row < Sq) {
+    uint2 pk[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv));
-    }
+    for (int db = 0; db < 4; ++db)
+      pk[db] = pack4_bf16_bits(R.O[db][i][0] * inv, R.O[db][i][1] * inv, R.O[db][i][2] * inv, R.O[db][i][3] * inv);
+    store_tile_rows(ob + (size_t)(row < Sq ? row : 0) * HD, row < Sq, grp, pk);
   }
 }
 
@@ -665,12 +664,11 @@ __device__ __forceinline__ void duo_wave(DuoLds& sm, const unsigned short* __res
   for (int i = 0; i < NQB; ++i) {
     const float inv = 1.0f / L[i][0];
     const int row = q0 + 16 * i + col;
-    if (row < Sq) {
+    uint2 pk[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(O[db][i][0] * inv, O[db][i][1] * inv, O[db][i][2] * inv, O[db][i][3] * inv));
-    }
+    for (int db = 0; db < 4; ++db)
+      pk[db] = pack4_bf16_bits(O[db][i][0] * inv, O[db][i][1] * inv, O[db][i][2] * inv, O[db][i][3] * inv);
+    store_tile_rows(ob + (size_t)(row < Sq ? row : 0) * HD, row < Sq, grp, pk);
   }
 }
 
@@ -936,12 +934,10 @@ __global__ __launch_bounds__(64 * NW) void xattn_bf16(const unsigned short* __re
     }
     const float inv = 1.0f / l;
     const int row = q0 + col;
-    if (row < Sq) {
+    uint2 pk[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        st8(ob + (size_t)row * HD + 16 * db + 4 * grp,
-            pack4_bf16_bits(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv));
-    }
+    for (int db = 0; db < 4; ++db) pk[db] = pack4_bf16_bits(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv);
+    store_tile_rows(ob + (size_t)(row < Sq ? row : 0) * HD, row < Sq, grp, pk);
     if constexpr (ONLINE) {
       Qc[0] = Qn[0];
       Qc[1] = Qn[1];

@@ -515,16 +515,18 @@ void diff_band(DiffArgs a, int nblk, int nstrip) {
     float l1, l2;
     band_branch<NKB, NR>(K1s, Vs, s0, Q1, band, edge, jbase, S, a.c, col, grp, ones, O1, l1);
     band_branch<NKB, NR>(K2s, Vs, s0, Q2, band, edge, jbase, S, a.c, col, grp, ones, O2, l2);
-    if (p < S) {
+    {
+      // every lane takes part in the store's lane exchange; only rows below S are written
       const float i1 = __builtin_amdgcn_rcpf(l1), i2 = lam * __builtin_amdgcn_rcpf(l2);
-      unsigned short* orow = oslice + (size_t)p * a.st[TO];
+      uint2 pk[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         f32x4 r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[e] = pin(O1[db][e] * i1) - pin(O2[db][e] * i2);
-        st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
+        pk[db] = pack4_bf16_bits(r[0], r[1], r[2], r[3]);
       }
+      store_tile_rows(oslice + (size_t)(p < S ? p : 0) * a.st[TO], p < S, grp, pk);
     }
     if (more) {
       __syncthreads();  // every wave is done with the rows about to be replaced
@@ -963,18 +965,18 @@ void diff_flash_duo(DiffArgs a, int nqb) {
 #pragma unroll
     for (int i = 0; i < NQB; ++i) {
       const int p = q0 + 16 * i + col;
-      if (p < S) {
-        const float i1 = 1.0f / L[i][0];
-        unsigned short* orow = a.o + slice_at(a, TO, bb, h) + (size_t)p * a.st[TO];
+      // every lane takes part in the store's lane exchange; only rows below S are written
+      const float i1 = 1.0f / L[i][0];
+      uint2 pk[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const f32x4 x = X[((wq * NQB + i) * 4 + db) * 64 + lane];
-          f32x4 r;
+      for (int db = 0; db < 4; ++db) {
+        const f32x4 x = X[((wq * NQB + i) * 4 + db) * 64 + lane];
+        f32x4 r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = pin(O[db][i][e] * i1) - x[e];
-          st8(orow + 16 * db + 4 * grp, pack4_bf16_bits(r[0], r[1], r[2], r[3]));
-        }
+        for (int e = 0; e < 4; ++e) r[e] = pin(O[db][i][e] * i1) - x[e];
+        pk[db] = pack4_bf16_bits(r[0], r[1], r[2], r[3]);
       }
+      store_tile_rows(a.o + slice_at(a, TO, bb, h) + (size_t)(p < S ? p : 0) * a.st[TO], p < S, grp, pk);
     }
   }
 }

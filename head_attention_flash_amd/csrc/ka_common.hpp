@@ -201,6 +201,24 @@ __device__ __forceinline__ uint2 pack4_bf16_bits(float a, float b, float c, floa
   return __builtin_bit_cast(uint2, v);
 }
 
+// Store one 16-query x 64-dim output tile held in the O^T C layout (lane: query l % 16, dims
+// 16 db + 4 (l / 16) + e) as 16 contiguous bytes per lane: one v_permlane16_swap per register
+// trades dims between the lane groups l / 16 = 0, 1 (and 2, 3), so that group g holds dims
+// 8 (g >> 1) + 16 (g & 1) + 32 h .. + 7 for h = 0, 1; a store instruction then writes 64
+// contiguous bytes of each row.  row_ptr: the lane's output row (dims 0..63); ok: row exists.
+__device__ __forceinline__ void store_tile_rows(unsigned short* row_ptr, bool ok, int grp, const uint2 (&p)[4]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint2 x = p[2 * h], y = p[2 * h + 1];
+    const u32x2 s0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+    const u32x2 s1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+    // s?[0]: the new first operand (own dims in groups 0 and 2, the partner's in 1 and 3),
+    // s?[1]: the new second operand (the partner's in groups 0 and 2, own in 1 and 3)
+    const uint4 v = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+    if (ok) st16(row_ptr + 32 * h + 8 * (grp >> 1) + 16 * (grp & 1), v);
+  }
+}
+
 // DyT: gamma * tanh(alpha x) + beta.  With tanh(y) = 1 - 2/(1 + e^{2y}) this is
 // (gamma + beta) - 2 gamma / (1 + e^{2 alpha x}): one exp, one reciprocal, one FMA,
 // given k2a = 2 log2(e) alpha, gpb = gamma + beta and m2g = -2 gamma.  It saturates
