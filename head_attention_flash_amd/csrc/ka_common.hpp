@@ -206,6 +206,8 @@ __device__ __forceinline__ uint2 pack4_bf16_bits(float a, float b, float c, floa
 // trades dims between the lane groups l / 16 = 0, 1 (and 2, 3), so that group g holds dims
 // 8 (g >> 1) + 16 (g & 1) + 32 h .. + 7 for h = 0, 1; a store instruction then writes 64
 // contiguous bytes of each row.  row_ptr: the lane's output row (dims 0..63); ok: row exists.
+// Every lane of the wave calls it (the swap reads the partner lane's registers); the four lanes
+// of a query share its ok, so values only move between lanes that store together or not at all.
 __device__ __forceinline__ void store_tile_rows(unsigned short* row_ptr, bool ok, int grp, const uint2 (&p)[4]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
